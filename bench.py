@@ -1,0 +1,170 @@
+"""Benchmark of the W4A16 MoE expert layer on one MI355X.
+
+One step = one pass of the whole layer over one batch: alignment of the
+top-k routing, W13 grouped GEMM with fused dequantisation and SwiGLU, W2
+grouped GEMM with the top-k-weighted scatter-add, and the BF16 convert
+(the indexed entry point with internal alignment). Inputs are seeded
+synthetic tensors already resident in HBM when timing starts.
+
+Default workload: Kimi-K2.x-shaped decode, indexed layout (384 experts,
+hidden 7168, intermediate 2048, 448 tokens, top-8).
+
+Prints one JSON line (rank 0). Per-kernel durations come from HIP events the
+library records around each launch on the launch stream during the timed
+steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer µs/call; decode weight GB/s & prefill TFLOP/s as % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense BF16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1, help="index into synth.WORKLOADS (indexed layouts)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-experts", type=int, default=8, help="experts in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(a, torch, np):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def cpu_baseline(wl, w, x, ids, tw, n_experts):
+    """The oracle as it stands, on a bounded sample: experts 0..n-1 with all
+    the rows routed to them (dequantisation, both GEMMs, SwiGLU and their
+    share of the combine), scaled by E / n to a whole call."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    experts = list(range(min(n_experts, wl.E)))
+    t0 = time.perf_counter()
+    for e in experts:
+        rows = np.argwhere(ids == e)
+        if rows.size == 0:
+            continue
+        w13 = O.dequant(w[0][e], w[1][e])
+        w2 = O.dequant(w[2][e], w[3][e])
+        _, _, y = O.expert_ffn(x[rows[:, 0]], w13, w2)
+        _ = tw[rows[:, 0], rows[:, 1]][:, None].astype(np.float64) * y
+    dt = time.perf_counter() - t0
+    per_call_us = dt * 1e6 * wl.E / len(experts)
+    return {"value": per_call_us, "unit": "us/call", "cores": int(threads), "kind": "oracle",
+            "sample": f"experts 0..{len(experts) - 1} of {wl.E} with all their routed rows "
+                      f"({dt:.1f} s), scaled x{wl.E / len(experts):.0f} to one call"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a16_int4_grouped_amd as M
+
+    wl = synth.WORKLOADS[args.workload]
+    if wl.layout != "indexed":
+        sys.exit("bench.py times the indexed layout workloads")
+    log(f"workload {wl.name}: generating inputs")
+    t = time.time()
+    w = synth.stacked_weights(wl)
+    x = synth.activations(wl.iseed, wl.T, wl.H)
+    ids, tw = synth.routing(wl)
+    log(f"  generated in {time.time() - t:.1f} s; uploading and preparing")
+    dw = [to_dev(a, torch, np) for a in w]
+    h = M.PreparedWeights(*dw, mode="indexed")
+    del dw
+    torch.cuda.empty_cache()
+    x_d, ids_d, tw_d = to_dev(x, torch, np), to_dev(ids, torch, np), to_dev(tw, torch, np)
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(h.workspace_bytes(wl.T, wl.topk, wl.T), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    log(f"  schedule: {h.describe(wl.T, wl.topk)}")
+
+    def step():
+        h.indexed(x_d, ids_d, tw_d, out=out, ws=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    M.profile_reset()
+    M.profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    M.profile_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    kernels = M.profile_read()
+    log("  kernels (avg us): " + ", ".join(f"{k}={v[1] / v[0] * 1e3:.1f}" for k, v in sorted(kernels.items())))
+
+    # roofline of the dominant kernel: W13 grouped GEMM, bound by HBM on its
+    # packed weight bytes (every touched expert's W13 is streamed once)
+    touched = int(np.unique(ids[(ids >= 0) & (ids < wl.E)]).size)
+    dom = "gemm_w13_small_m"
+    n, tot_ms = kernels.get(dom, (0, 0.0))
+    dom_us = tot_ms / max(n, 1) * 1e3
+    w13_bytes = touched * wl.H * wl.I           # 2I rows x H/2 bytes
+    achieved = w13_bytes / (dom_us * 1e-6) / 1e9 if dom_us > 0 else 0.0
+    layer_packed = touched * 1.5 * wl.H * wl.I
+    result = {
+        "metric": METRIC,
+        "value": ms * 1e3,
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layout": wl.layout, "experts": wl.E, "hidden": wl.H,
+                   "intermediate": wl.I, "tokens": wl.T, "topk": wl.topk,
+                   "weights": "uint4 g32 bf16-scale", "layer_packed_GBps": layer_packed / (ms * 1e-3) / 1e9,
+                   "layer_packed_frac_hbm": layer_packed / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "avg_us": dom_us, "bytes_per_launch": w13_bytes},
+        "kernels_avg_us": {k: v[1] / v[0] * 1e3 for k, v in kernels.items()},
+    }
+    if not args.no_cpu_baseline:
+        log("  timing the CPU oracle sample")
+        result["cpu_baseline"] = cpu_baseline(wl, w, x, ids, tw, args.cpu_experts)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,296 @@
+/*
+ * moe_w4a16.h -- C ABI of the W4A16 mixture-of-experts expert layer for
+ * MI355X (gfx950).
+ *
+ * The layer (Chord page: "vLLM x Novita AI release Chord, an INT4 MoE
+ * operator for Kimi K2.x", sections "TL;DR", "Indexed kernels", "Grouped SM90
+ * kernels"):
+ *   activations BF16; expert weights uint4 packed eight per int32 word, low
+ *   nibble first along K, one BF16 scale per group of 32 along K, zero point
+ *   8, dequantised subtract-then-scale w = bf16((q - 8) * s);
+ *   per routed row: h = x . W13^T (gate = rows [0, I), up = rows [I, 2I)),
+ *   a = bf16(silu(gate) * up), y = a . W2^T, and a top-k-weighted combine
+ *   out[t] = sum_j w[t, j] * y(t, j) (indexed layout, and contiguous layout
+ *   with row_src).
+ *
+ * Conventions for every call:
+ *   - bf16 values travel as uint16_t bit patterns.
+ *   - "device" pointers point to GPU memory (hipMalloc / torch tensors) and
+ *     stay owned by the caller; the library never allocates or frees device
+ *     memory. "host" pointers point to CPU memory.
+ *   - stream is a hipStream_t (NULL = the default stream). Every device
+ *     operation is enqueued on it without host synchronisation, except
+ *     moe_prepare_weights (load time), which synchronises once.
+ *   - Every argument is validated on the host before anything is enqueued;
+ *     on an error nothing is enqueued and moe_last_error() describes it.
+ *   - Device-side data errors cannot be seen without a synchronisation:
+ *     expert ids outside [0, E) route nowhere, masked_m is clamped to
+ *     [0, max_m], and a contiguous row whose m_index is outside [0, E) is
+ *     treated as padding.
+ *   - Calls that share a workspace or routing buffer on one stream are
+ *     ordered by the stream; concurrent use of one buffer from two streams
+ *     races.
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_W4A16_ABI_VERSION 1
+
+typedef void* moe_stream_t; /* a hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,        /* a NULL pointer, a bad size or count */
+  MOE_ERR_UNSUPPORTED_SCHEMA = 2, /* quantisation schema not uint4/g32/BF16/zp8 */
+  MOE_ERR_MODE_MISMATCH = 3,      /* weights prepared for another layout */
+  MOE_ERR_OVERRIDE_REJECTED = 4,  /* tuning override on a grouped layout */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 5,/* workspace / routing / prepared buffer */
+  MOE_ERR_HIP = 6,                /* a HIP runtime call failed */
+  MOE_ERR_ROUTING_MISMATCH = 7    /* routing buffer made for other shapes */
+} moe_status_t;
+
+/* Layout a set of prepared weights serves (Chord page, "Grouped SM90
+ * kernels", Fig. 3: where the padding lives). The layout is recorded in the
+ * prepared weights and checked by every entry point. */
+typedef enum {
+  MOE_MODE_INDEXED = 0,    /* unpadded activations, routing with sentinels */
+  MOE_MODE_CONTIGUOUS = 1, /* each expert padded to a 128-row boundary */
+  MOE_MODE_MASKED = 2      /* fixed per-expert row budget, masked_m counts */
+} moe_mode_t;
+
+enum { MOE_SCALE_BF16 = 1 };
+enum { MOE_PACK_INT32_LOW_NIBBLE_FIRST_K = 1 };
+
+/* The quantisation schema and shapes of one MoE layer. Only uint4 (bits = 4),
+ * group_size = 32, zero_point = 8, BF16 scales and low-nibble-first int32
+ * packing along K are supported (Chord page, "vLLM integration": the schema
+ * is uint4, group-32, BF16 scales; other schemas fail at load). hidden and
+ * inter must be positive multiples of 32. */
+typedef struct {
+  int32_t num_experts; /* E, 1..4096 */
+  int32_t hidden;      /* H: K of W13, N of W2 */
+  int32_t inter;       /* I: W13 has N = 2I rows (gate | up), W2 has K = I */
+  int32_t bits;        /* 4 */
+  int32_t group_size;  /* 32 */
+  int32_t zero_point;  /* 8 */
+  int32_t scale_dtype; /* MOE_SCALE_BF16 */
+  int32_t pack_order;  /* MOE_PACK_INT32_LOW_NIBBLE_FIRST_K */
+  int32_t mode;        /* moe_mode_t */
+} moe_weight_desc_t;
+
+/* Per-call schedule overrides, accepted by the indexed entry point only
+ * (Chord page, "Grouped SM90 kernels": grouped dispatch owns its layout
+ * search and rejects the indexed block_m / tuning overrides). A zero field
+ * means "choose automatically". */
+typedef struct {
+  int32_t block_m;  /* alignment block (rows): 16, 32, 64 or 128 */
+  int32_t schedule; /* 0 auto, 1 small-M (decode), 2 large-M (prefill) */
+  int32_t reserved0;
+  int32_t reserved1;
+} moe_tuning_t;
+
+typedef struct moe_weights moe_weights_t; /* opaque host handle */
+
+/* ---- library ---------------------------------------------------------- */
+
+/* MOE_W4A16_ABI_VERSION of the loaded library. */
+int moe_abi_version(void);
+
+/* Thread-local description of the last error of this thread ("" if none).
+ * The string stays valid until the next call on the same thread. */
+const char* moe_last_error(void);
+
+/* Static name of a status code. */
+const char* moe_status_string(int status);
+
+/* ---- load time ---------------------------------------------------------- */
+
+/* Bytes of device memory moe_prepare_weights needs for desc, or 0 if desc is
+ * invalid or unsupported (moe_last_error says why). */
+size_t moe_prepared_bytes(const moe_weight_desc_t* desc);
+
+/* Repack canonical weights into the prepared layout and fix the layout mode
+ * (Chord page, "Indexed kernels": configurations and weight layouts are
+ * fixed at model load, before packing; "Grouped SM90 kernels": the forward
+ * path sees pre-permuted INT4 bytes and re-tiled scales).
+ *   w13_q  device int32 [E, 2I, H/8]  rows [0,I) gate, [I,2I) up
+ *   w13_s  device bf16  [E, 2I, H/32]
+ *   w2_q   device int32 [E, H, I/8]
+ *   w2_s   device bf16  [E, H, I/32]
+ *   prepared  device buffer of prepared_bytes >= moe_prepared_bytes(desc),
+ *             256-byte aligned, owned by the caller, kept alive and unchanged
+ *             while the handle is used. The canonical inputs may be freed
+ *             after the call returns.
+ *   out    host: receives a new handle (release with moe_release_weights).
+ * Synchronises `stream` once. Errors: INVALID_ARG, UNSUPPORTED_SCHEMA (also
+ * when a scale is NaN, infinite or of magnitude >= 2^125, checked on the
+ * device), WORKSPACE_TOO_SMALL, HIP. */
+moe_status_t moe_prepare_weights(const moe_weight_desc_t* desc, const int32_t* w13_q,
+                                 const uint16_t* w13_s, const int32_t* w2_q,
+                                 const uint16_t* w2_s, void* prepared, size_t prepared_bytes,
+                                 moe_stream_t stream, moe_weights_t** out);
+
+/* Free a host handle (not the caller's prepared buffer). NULL is ignored. */
+void moe_release_weights(moe_weights_t* h);
+
+/* A handle without weights, for sizing buffers before the weights are
+ * loaded: size queries (moe_routing_bytes, moe_routing_layout,
+ * moe_workspace_bytes) and moe_describe work; every call that would enqueue
+ * device work validates its arguments as usual and then returns
+ * MOE_ERR_INVALID_ARG. Returns NULL (moe_last_error says why) for an invalid
+ * or unsupported desc. Release with moe_release_weights. Makes no HIP call. */
+moe_weights_t* moe_plan_create(const moe_weight_desc_t* desc);
+
+/* ---- routing (indexed layout) -------------------------------------------- */
+
+/* Alignment block (rows) the indexed entry point uses for T tokens x topk
+ * with these overrides (NULL = none): the per-call schedule refined by
+ * tokens per expert (Chord page, "H200 prefill and TP8"). 0 on error. */
+int32_t moe_routing_block(const moe_weights_t* h, int32_t T, int32_t topk,
+                          const moe_tuning_t* ovr);
+
+/* Bytes of the routing buffer for (T, topk, ovr), 0 on error. */
+size_t moe_routing_bytes(const moe_weights_t* h, int32_t T, int32_t topk,
+                         const moe_tuning_t* ovr);
+
+/* Layout of a routing buffer, in int32 elements from its start. */
+typedef struct {
+  int32_t block;        /* alignment block B */
+  int32_t cap;          /* T*topk + E*(B-1): slots in sorted_ids */
+  int32_t nblocks;      /* ceil(cap / B): entries of block_expert */
+  int32_t sentinel;     /* T*topk */
+  int64_t off_header;   /* int32[16]; [7] = total padded rows (device-written) */
+  int64_t off_counts;   /* int32[E]   rows per expert */
+  int64_t off_offsets;  /* int32[E+1] exclusive scan of padded counts */
+  int64_t off_sorted;   /* int32[cap] flat row t*topk+j, or sentinel */
+  int64_t off_block_expert; /* int32[nblocks] expert of block b, -1 past total */
+  int64_t off_scratch;  /* internal scratch */
+  int64_t total_ints;
+} moe_routing_layout_t;
+
+moe_status_t moe_routing_layout(const moe_weights_t* h, int32_t T, int32_t topk,
+                                const moe_tuning_t* ovr, moe_routing_layout_t* out);
+
+/* Token -> expert alignment for the indexed layout (Chord page, "Grouped SM90
+ * kernels", Fig. 3: activations stay unpadded, the routing indices carry pad
+ * sentinels). Bit-exact and deterministic:
+ *   counts[e] = rows routed to e; offsets = exclusive scan of
+ *   ceil(counts/B)*B; sorted_ids[offsets[e] + r] = r-th flat row of e in
+ *   ascending t*topk+j order; all other slots hold the sentinel T*topk;
+ *   block_expert[b] = expert owning block b, -1 past the total.
+ *   topk_ids  device int32 [T, topk]
+ *   routing   device buffer of moe_routing_bytes(h, T, topk, ovr) bytes,
+ *             4-byte aligned.
+ * Errors: INVALID_ARG, MODE_MISMATCH (handle not INDEXED),
+ * WORKSPACE_TOO_SMALL, HIP. T = 0 is valid and writes an empty routing. */
+moe_status_t moe_align(const moe_weights_t* h, const int32_t* topk_ids, int32_t T, int32_t topk,
+                       const moe_tuning_t* ovr, void* routing, size_t routing_bytes,
+                       moe_stream_t stream);
+
+/* Gather x rows into the aligned order (the contiguous layout's producer):
+ *   a_out      device bf16 [cap, H]: row p = x[sorted_ids[p] / topk], zero
+ *              for sentinel slots
+ *   m_indices  device int32 [cap]: expert of row p, -1 for sentinel slots
+ *   row_src    device int32 [cap]: sorted_ids[p], -1 for sentinel slots
+ * Any of the three outputs may be NULL. routing must come from moe_align
+ * with the same (T, topk, ovr). */
+moe_status_t moe_permute(const moe_weights_t* h, const uint16_t* x, int32_t T, int32_t topk,
+                         const moe_tuning_t* ovr, const void* routing, uint16_t* a_out,
+                         int32_t* m_indices, int32_t* row_src, moe_stream_t stream);
+
+/* ---- the layer ------------------------------------------------------------ */
+
+/* Workspace bytes for one call, 0 on error.
+ *   indexed:    rows = T (tokens), topk = top-k
+ *   contiguous: rows = M_pad, topk = top-k if row_src will be passed (T via
+ *               tokens), else 0
+ *   masked:     rows = max_m, topk ignored
+ * `tokens` is T for the combine accumulator (indexed; contiguous with
+ * row_src), ignored otherwise. ovr: the indexed call's overrides (they set
+ * the alignment block and so the routing capacity), NULL otherwise. */
+size_t moe_workspace_bytes(const moe_weights_t* h, int32_t mode, int32_t rows, int32_t topk,
+                           int32_t tokens, const moe_tuning_t* ovr);
+
+/* Indexed layout. Unpadded activations, routing by moe_align.
+ *   x        device bf16 [T, H]
+ *   topk_ids device int32 [T, topk], topk_w device float [T, topk]
+ *   routing  device buffer from moe_align(h, topk_ids, T, topk, ovr, ...) on
+ *            this stream, or NULL to align internally (in the workspace)
+ *   out      device bf16 [T, H] (fully written; tokens routed nowhere get 0)
+ *   ws       device workspace of ws_bytes >= moe_workspace_bytes(h,
+ *            MOE_MODE_INDEXED, T, topk, T, ovr), 256-byte aligned
+ *   ovr      NULL or overrides (block_m, schedule)
+ * Errors: INVALID_ARG, MODE_MISMATCH, WORKSPACE_TOO_SMALL, HIP. */
+moe_status_t moe_w4a16_indexed(const moe_weights_t* h, const uint16_t* x, int32_t T, int32_t topk,
+                               const int32_t* topk_ids, const float* topk_w, const void* routing,
+                               uint16_t* out, void* ws, size_t ws_bytes, const moe_tuning_t* ovr,
+                               moe_stream_t stream);
+
+/* Contiguous layout (Chord page, "Grouped SM90 kernels", Fig. 3).
+ *   a          device bf16 [M_pad, H], M_pad % 128 == 0; each expert's rows
+ *              contiguous and starting on a 128-row boundary
+ *   m_indices  device int32 [M_pad]: expert of each row, -1 for padding
+ *   row_src    device int32 [M_pad] (t*topk+j, -1 for padding) or NULL
+ *   topk_w     device float [T, topk], needed with row_src
+ *   out        row_src ? bf16 [T, H] combined : bf16 [M_pad, H] per row
+ *              (pad rows unspecified)
+ *   ovr        must be NULL (OVERRIDE_REJECTED otherwise)
+ * Errors: INVALID_ARG, MODE_MISMATCH, OVERRIDE_REJECTED,
+ * WORKSPACE_TOO_SMALL, HIP. */
+moe_status_t moe_w4a16_contiguous(const moe_weights_t* h, const uint16_t* a, int32_t M_pad,
+                                  const int32_t* m_indices, const int32_t* row_src,
+                                  const float* topk_w, int32_t T, int32_t topk, uint16_t* out,
+                                  void* ws, size_t ws_bytes, const moe_tuning_t* ovr,
+                                  moe_stream_t stream);
+
+/* Masked layout (Chord page, "Grouped SM90 kernels": expected_m is a
+ * positive integer that picks the launch, masked_m holds the valid count
+ * per expert, the output is flat even for a 3-D a3, rows past the valid
+ * count are to be ignored).
+ *   a3         device bf16 [E, max_m, H]
+ *   masked_m   device int32 [E] (clamped to [0, max_m])
+ *   expected_m > 0: expected rows per expert, picks the schedule only
+ *   out        device bf16 [E * max_m, H]; rows >= masked_m[e] unspecified
+ *   ovr        must be NULL
+ * Errors: INVALID_ARG (also expected_m <= 0), MODE_MISMATCH,
+ * OVERRIDE_REJECTED, WORKSPACE_TOO_SMALL, HIP. */
+moe_status_t moe_w4a16_masked(const moe_weights_t* h, const uint16_t* a3, int32_t max_m,
+                              const int32_t* masked_m, int32_t expected_m, uint16_t* out,
+                              void* ws, size_t ws_bytes, const moe_tuning_t* ovr,
+                              moe_stream_t stream);
+
+/* ---- inspection ------------------------------------------------------------ */
+
+/* Dequantise one expert's prepared matrix back to canonical order with the
+ * same device routine the GEMMs use: which = 13 -> out bf16 [2I, H],
+ * which = 2 -> out bf16 [H, I]. */
+moe_status_t moe_dequant_weights(const moe_weights_t* h, int32_t which, int32_t expert,
+                                 uint16_t* out, moe_stream_t stream);
+
+/* Write a one-line text description of the schedule a call with these
+ * shapes would use (layout, rows per expert, kernel variant, tiles, grid).
+ * mode/rows/topk as for moe_workspace_bytes; expected_m for masked.
+ * Returns the length written (excluding NUL), or -1. */
+int moe_describe(const moe_weights_t* h, int32_t mode, int32_t rows, int32_t topk,
+                 int32_t expected_m, const moe_tuning_t* ovr, char* buf, size_t n);
+
+/* Kernel timing. While enabled, every kernel the library enqueues is
+ * bracketed by HIP events on its stream. moe_profile_read synchronises those
+ * events and writes lines "name launches total_ms\n" (totals since the last
+ * reset) into buf; it returns the length written or -1. */
+moe_status_t moe_profile_enable(int enable);
+void moe_profile_reset(void);
+int moe_profile_read(char* buf, size_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H */

@@ -91,11 +91,18 @@ def dequant(words, scale_bits) -> np.ndarray:
     order that the Chord page's decode kernel keeps; "H200 and Blackwell
     indexed decode"). Returns uint16 BF16 bit patterns [..., N, K].
     """
-    q = unpack_nibbles(words).astype(np.float64) - 8.0
-    s = bf16_to_f64(scale_bits)
-    s_full = np.repeat(s, 32, axis=-1)
-    assert s_full.shape == q.shape, (s_full.shape, q.shape)
-    return bf16_round(q * s_full)
+    words = np.asarray(words)
+    scale_bits = np.asarray(scale_bits)
+    assert words.shape[:-1] == scale_bits.shape[:-1] and words.shape[-1] == 4 * scale_bits.shape[-1]
+    if words.ndim > 2 or words.shape[0] <= 64:
+        q = unpack_nibbles(words).astype(np.float64) - 8.0
+        s_full = np.repeat(bf16_to_f64(scale_bits), 32, axis=-1)
+        return bf16_round(q * s_full)
+    # rows are independent: work on 64 at a time to keep temporaries small
+    out = np.empty((words.shape[0], words.shape[1] * 8), dtype=np.uint16)
+    for r in range(0, words.shape[0], 64):
+        out[r:r + 64] = dequant(words[r:r + 64], scale_bits[r:r + 64])
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -1,0 +1,95 @@
+"""Helpers for the GPU tests: moving seeded inputs to the device, preparing
+weights through the C ABI, and the tolerance check.
+
+Inputs come from synth/, expected values from oracle/ (on the CPU); nothing
+here computes any part of the layer.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+# layer-output tolerance: relative Frobenius error and max-abs error over rms(ref)
+REL_FRO_TOL = 5e-3
+MAX_ABS_TOL = 3e-2
+
+
+def cuda_available():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def require_gpu():
+    if not cuda_available():
+        pytest.fail("GPU test run without a GPU")
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_dev(bits: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def i32_dev(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def f32_dev(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def bits_host(t) -> np.ndarray:
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f64_host(t) -> np.ndarray:
+    import torch
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def weights_dev(w13_q, w13_s, w2_q, w2_s):
+    return (i32_dev(w13_q), bf16_dev(w13_s), i32_dev(w2_q), bf16_dev(w2_s))
+
+
+def prepare(weights_np, mode="indexed", dev_weights=None):
+    import w4a16_int4_grouped_amd as M
+    dw = dev_weights if dev_weights is not None else weights_dev(*weights_np)
+    return M.PreparedWeights(*dw, mode=mode)
+
+
+def check_tol(got, ref, what=""):
+    """Layer-output parity: relFro <= 5e-3 and max-abs <= 3e-2 * rms(ref)."""
+    from oracle import compare
+    m = compare(got, ref)
+    log(f"  parity {what}: rel_fro={m['rel_fro']:.3e} max_abs/rms={m['max_abs_over_rms']:.3e} "
+        f"bf16_floor={m['bf16_floor']:.3e} n={m['n']}")
+    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+    assert m["rel_fro"] <= REL_FRO_TOL, (what, m)
+    assert m["max_abs_over_rms"] <= MAX_ABS_TOL, (what, m)
+    return m
+
+
+def a_mismatch(got_bits: np.ndarray, ref_bits: np.ndarray, what=""):
+    """Intermediate `a` (BF16): fraction of elements that differ and the
+    largest difference in units of the last place."""
+    g = got_bits.astype(np.int32)
+    r = ref_bits.astype(np.int32)
+    # order-preserving integer view of bf16
+    def ordered(v):
+        return np.where(v & 0x8000, 0x8000 - (v & 0x7FFF), 0x8000 + v)
+    diff = np.abs(ordered(g) - ordered(r))
+    frac = float(np.mean(diff != 0)) if diff.size else 0.0
+    mx = int(diff.max()) if diff.size else 0
+    log(f"  intermediate a {what}: mismatch fraction {frac:.2e}, max ulp {mx}")
+    return frac, mx

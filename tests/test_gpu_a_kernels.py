@@ -1,0 +1,211 @@
+"""GPU parity of the bit-exact steps: alignment, permutation, dequantisation,
+and the MFMA fragment mapping (one-hot weights), through the C ABI."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import moe_oracle as O
+from tests.gpu_util import (bf16_dev, bits_host, check_tol, f32_dev, i32_dev, log, prepare,
+                            require_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def tiny_weights(E, H, I, seed=0):
+    r = np.random.default_rng(seed)
+    w13_q = r.integers(0, 2**32, (E, 2 * I, H // 8), dtype=np.uint32).view(np.int32)
+    w2_q = r.integers(0, 2**32, (E, H, I // 8), dtype=np.uint32).view(np.int32)
+    w13_s = synth._to_bf16_bits((np.abs(r.standard_normal((E, 2 * I, H // 32))) * 0.02 + 1e-3).astype(np.float32))
+    w2_s = synth._to_bf16_bits((np.abs(r.standard_normal((E, H, I // 32))) * 0.02 + 1e-3).astype(np.float32))
+    return w13_q, w13_s, w2_q, w2_s
+
+
+ROUTINGS = [
+    # (name, E, T, topk, kind)
+    ("cfg0", 8, 32, 2, "softmax"),
+    ("cfg1", 384, 448, 8, "softmax"),
+    ("cfg2-zipf", 384, 8192, 8, "zipf"),
+    ("cfg4", 384, 4096, 8, "softmax"),
+    ("one-token", 5, 1, 3, "softmax"),
+    ("ragged", 7, 1001, 3, "softmax"),
+]
+
+
+def routing_ids(E, T, topk, kind, seed):
+    if kind == "zipf":
+        return synth.zipf_routing(seed, T, E, topk)[0]
+    return synth.softmax_routing(seed, T, E, topk)[0]
+
+
+@pytest.fixture(scope="module")
+def handles():
+    require_gpu()
+    cache = {}
+
+    def get(E):
+        if E not in cache:
+            cache[E] = prepare(tiny_weights(E, 64, 32), "indexed")
+        return cache[E]
+    return get
+
+
+def read_routing(h, routing, T, topk, ovr=None):
+    lay = h.routing_layout(T, topk, ovr)
+    r = routing.cpu().numpy()
+    E = h.E
+    return dict(counts=r[lay.off_counts:lay.off_counts + E],
+                offsets=r[lay.off_offsets:lay.off_offsets + E + 1],
+                sorted_ids=r[lay.off_sorted:lay.off_sorted + lay.cap],
+                block_expert=r[lay.off_block_expert:lay.off_block_expert + lay.nblocks],
+                total=int(r[7]), block=lay.block)
+
+
+@pytest.mark.parametrize("name,E,T,topk,kind", ROUTINGS)
+@pytest.mark.parametrize("block_m", [0, 16, 64, 128])
+def test_align_bit_exact(handles, name, E, T, topk, kind, block_m):
+    h = handles(E)
+    ids = routing_ids(E, T, topk, kind, seed=200 + T)
+    if name == "ragged":
+        ids[::17, 0] = -1          # dropped rows
+        ids[5, 1] = E              # out of range
+    ovr = {"block_m": block_m} if block_m else None
+    ids_d = i32_dev(ids)
+    first = None
+    for rep in range(3):
+        routing = h.align(ids_d, ovr=ovr)
+        got = read_routing(h, routing, T, topk, ovr)
+        if first is None:
+            first = got
+        else:
+            for k in ("sorted_ids", "offsets"):
+                assert np.array_equal(got[k], first[k]), f"nondeterministic {k}"
+    ref = O.align(ids, E, got["block"])
+    log(f"  align {name} B={got['block']} total={ref['total']} cap={ref['cap']}")
+    for k in ("counts", "offsets", "sorted_ids", "block_expert"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert got["total"] == ref["total"]
+
+
+def test_align_empty(handles):
+    import torch
+    h = handles(8)
+    ids = torch.zeros((0, 2), dtype=torch.int32, device="cuda")
+    routing = h.align(ids)
+    got = read_routing(h, routing, 0, 2)
+    ref = O.align(np.zeros((0, 2), np.int32), 8, got["block"])
+    for k in ("counts", "offsets", "sorted_ids", "block_expert"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+@pytest.mark.parametrize("block_m", [16, 128])
+def test_permute_bit_exact(handles, block_m):
+    E, T, topk = 7, 300, 3
+    h = handles(E)
+    ids = routing_ids(E, T, topk, "softmax", 5)
+    x = synth.activations(9, T, 64)
+    ovr = {"block_m": block_m}
+    routing = h.align(i32_dev(ids), ovr=ovr)
+    a, m_idx, row_src = h.permute(bf16_dev(x), topk, routing, ovr=ovr)
+    al = O.align(ids, E, block_m)
+    assert np.array_equal(bits_host(a), O.permute(x, al, topk))
+    ok = al["sorted_ids"] < al["sentinel"]
+    m_ref = np.where(ok, np.repeat(al["block_expert"], block_m)[:al["cap"]], -1)
+    assert np.array_equal(m_idx.cpu().numpy(), m_ref)
+    assert np.array_equal(row_src.cpu().numpy(), np.where(ok, al["sorted_ids"], -1))
+
+
+def test_dequant_exhaustive_all_scales():
+    """Every finite BF16 scale below 2^125 in magnitude (plus zeros and
+    subnormals) against all 16 codes, through the GEMMs' device routine."""
+    require_gpu()
+    s_all = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    supported = (s_all & 0x7FFF) < 0x7E00
+    s = s_all[supported]
+    # one expert, W13 with N = 2I rows, K = H columns: N*(K/32) >= len(s)
+    H, I = 1024, 1024
+    N, G = 2 * I, H // 32
+    assert N * G >= s.size
+    scales = np.resize(s, N * G).reshape(N, G)
+    # every group of 32 holds each of the 16 codes twice
+    q = ((np.arange(H)[None, :] + np.arange(N)[:, None]) % 16).astype(np.uint32)
+    words = np.zeros((N, H // 8), dtype=np.uint32)
+    for i in range(8):
+        words |= q[:, i::8] << np.uint32(4 * i)
+    w13_q = words.view(np.int32)[None]
+    w13_s = scales[None]
+    w2 = tiny_weights(1, H, I, seed=3)
+    h = prepare((w13_q, w13_s, w2[2], w2[3]), "indexed")
+    got = bits_host(h.dequant(13, 0))
+    ref = O.dequant(w13_q[0], w13_s[0])
+    nan_ref = np.isnan(O.bf16_to_f64(ref))
+    assert not nan_ref.any()
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[0]}: got {got[tuple(bad[0])]:#x} ref {ref[tuple(bad[0])]:#x}"
+    got2 = bits_host(h.dequant(2, 0))
+    assert np.array_equal(got2, O.dequant(w2[2][0], w2[3][0]))
+
+
+def test_unsupported_scales_fail_at_load():
+    require_gpu()
+    import w4a16_int4_grouped_amd as M
+    w = list(tiny_weights(2, 64, 32))
+    for bad in (0x7F80, 0x7FC0, 0x7E00, 0xFE00):
+        w13_s = w[1].copy()
+        w13_s[1, 3, 1] = bad
+        with pytest.raises(M.MoeError) as ei:
+            prepare((w[0], w13_s, w[2], w[3]), "indexed")
+        assert ei.value.status == M.MOE_ERR_UNSUPPORTED_SCHEMA
+
+
+@pytest.mark.parametrize("cfg", [0, 4])
+def test_dequant_config_weights_bit_exact(cfg):
+    """The configs' own weights: every expert of config 0, sampled experts
+    (first, middle, last) of the TP8 shard."""
+    require_gpu()
+    wl = synth.WORKLOADS[cfg]
+    experts = list(range(wl.E)) if wl.E <= 8 else [0, wl.E // 2, wl.E - 1]
+    w = synth.stacked_weights(wl)
+    h = prepare(w, "indexed")
+    for e in experts:
+        assert np.array_equal(bits_host(h.dequant(13, e)), O.dequant(w[0][e], w[1][e])), (cfg, e, 13)
+        assert np.array_equal(bits_host(h.dequant(2, e)), O.dequant(w[2][e], w[3][e])), (cfg, e, 2)
+
+
+def onehot_weights(E, H, I):
+    """Row n has its single nonzero at k = (3n + 1) mod K (not symmetric, so
+    a transposed tile shows), and power-of-two scales that vary with the row,
+    the scale group and the expert."""
+    def mat(N, K, scale_bits):
+        q = np.full((N, K), 8, dtype=np.uint32)
+        q[np.arange(N), (3 * np.arange(N) + 1) % K] = 9
+        words = np.zeros((N, K // 8), dtype=np.uint32)
+        for i in range(8):
+            words |= q[:, i::8] << np.uint32(4 * i)
+        g = np.arange(K // 32)[None, :]
+        n = np.arange(N)[:, None]
+        s = (scale_bits + (((n + 3 * g) % 4) << 7)).astype(np.uint16)
+        return words.view(np.int32), s
+    w13 = [mat(2 * I, H, 0x3F80 - (e << 7)) for e in range(E)]
+    w2 = [mat(H, I, 0x3F00 + (e << 7)) for e in range(E)]
+    return (np.stack([a for a, _ in w13]), np.stack([b for _, b in w13]),
+            np.stack([a for a, _ in w2]), np.stack([b for _, b in w2]))
+
+
+def test_fragment_mapping_onehot():
+    """One nonzero term per dot product: any row/column/k/scale-group or
+    gate/up mix-up in the MFMA fragment layout is an O(1) error."""
+    require_gpu()
+    E, H, I, T, topk = 4, 256, 128, 19, 2
+    w = onehot_weights(E, H, I)
+    r = np.random.default_rng(4)
+    x = synth.activations(3, T, H)
+    ids = np.stack([r.permutation(E)[:topk] for _ in range(T)]).astype(np.int32)
+    tw = r.random((T, topk)).astype(np.float32)
+    h = prepare(w, "indexed")
+    out = h.indexed(bf16_dev(x), i32_dev(ids), f32_dev(tw))
+    ref = O.moe_indexed(x, ids, tw, w, E=E)
+    got = O.bf16_to_f64(bits_host(out))
+    # exact up to BF16 output rounding and FP32 silu
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    np.testing.assert_allclose(got, ref, rtol=2 ** -7, atol=1e-2 * rms)
+    check_tol(got, ref, "one-hot")

@@ -1,0 +1,834 @@
+// Host side of the C ABI: argument and schema validation (all before any
+// HIP call), the prepared-weight handle, schedule selection by rows per
+// expert with a memoised descriptor cache, workspace carving, launch
+// sequencing on the caller's stream, and optional per-kernel event timing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "moe_launch.h"
+#include "moe_layout.h"
+#include "moe_w4a16.h"
+
+using namespace moe;
+
+// --------------------------------------------------------------------------
+// Errors
+// --------------------------------------------------------------------------
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status_t ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+moe_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// --------------------------------------------------------------------------
+// Environment overrides, read once per prepared handle (part of the
+// descriptor key, like the tuning overrides the Chord page memoises with
+// each descriptor in "Grouped SM90 kernels").
+// --------------------------------------------------------------------------
+
+struct EnvOverrides {
+  int schedule = 0;   // MOE_W4A16_SCHEDULE: 0 auto, 1 small-M, 2 large-M
+  int nt = 0;         // MOE_W4A16_NT: token tiles per weight pass (1, 2, 4)
+  int log = 0;        // MOE_W4A16_LOG: print each new schedule
+  void read() {
+    auto geti = [](const char* k) {
+      const char* v = std::getenv(k);
+      return v ? std::atoi(v) : 0;
+    };
+    schedule = geti("MOE_W4A16_SCHEDULE");
+    nt = geti("MOE_W4A16_NT");
+    log = geti("MOE_W4A16_LOG");
+  }
+};
+
+// --------------------------------------------------------------------------
+// Kernel timing
+// --------------------------------------------------------------------------
+
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  struct Pending {
+    const char* name;
+    hipEvent_t a, b;
+  };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+  std::map<std::string, std::pair<long, double>> totals;
+
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void drain() {   // caller holds mu
+    for (auto& p : pending) {
+      float ms = 0.f;
+      (void)hipEventSynchronize(p.b);
+      (void)hipEventElapsedTime(&ms, p.a, p.b);
+      auto& t = totals[p.name];
+      t.first += 1;
+      t.second += ms;
+      pool.push_back(p.a);
+      pool.push_back(p.b);
+    }
+    pending.clear();
+  }
+};
+
+Profiler& prof() {
+  static Profiler* p = new Profiler();   // never destroyed: events outlive static teardown
+  return *p;
+}
+
+template <class F>
+hipError_t run(const char* name, hipStream_t s, F&& f) {
+  Profiler& P = prof();
+  bool on;
+  {
+    std::lock_guard<std::mutex> g(P.mu);
+    on = P.on;
+  }
+  if (!on) return f();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> g(P.mu);
+    if (P.pending.size() > 4096) P.drain();
+    a = P.get();
+    b = P.get();
+  }
+  if (a) (void)hipEventRecord(a, s);
+  hipError_t e = f();
+  if (b) (void)hipEventRecord(b, s);
+  if (a && b) {
+    std::lock_guard<std::mutex> g(P.mu);
+    P.pending.push_back({name, a, b});
+  }
+  return e;
+}
+
+// --------------------------------------------------------------------------
+// Schedules
+// --------------------------------------------------------------------------
+
+enum { SCHED_SMALL_M = 1, SCHED_LARGE_M = 2 };
+
+// Rows per expert at which the large-M schedule takes over (Chord page,
+// "Indexed kernels", Fig. 2 and "H200 prefill and TP8": about 80 tokens per
+// expert is where block_m starts to follow each expert's padded rows).
+constexpr int kLargeMRows = 80;
+
+struct Schedule {
+  int kind = SCHED_SMALL_M;
+  int block = 16;   // routing alignment block (indexed)
+  int nt = 1;       // 16-row token tiles per weight pass (small-M)
+  int rows = 0;     // rows per expert the choice was made for
+};
+
+int nt_for_rows(int rows) {
+  if (rows <= 16) return 1;
+  if (rows <= 32) return 2;
+  return 4;
+}
+
+}  // namespace
+
+struct moe_weights {
+  moe_weight_desc_t desc{};
+  PreparedLayout lay;
+  char* prepared = nullptr;
+  size_t prepared_bytes = 0;
+  int device = 0;
+  EnvOverrides env;
+  std::mutex mu;
+  std::unordered_map<uint64_t, Schedule> cache;
+};
+
+namespace {
+
+uint64_t key_of(int mode, int a, int b, const moe_tuning_t* o) {
+  uint64_t k = (uint64_t)(mode & 3);
+  k = k * 1000003u + (uint32_t)a;
+  k = k * 1000003u + (uint32_t)b;
+  if (o) {
+    k = k * 1000003u + (uint32_t)o->block_m;
+    k = k * 1000003u + (uint32_t)o->schedule;
+  }
+  return k;
+}
+
+// Indexed: rows per expert tok_e = ceil(T*topk / E) picks the schedule (the
+// Chord page's tok_e rule: tokens per expert, not total tokens).
+Schedule schedule_indexed(moe_weights* h, int T, int topk, const moe_tuning_t* ovr) {
+  const uint64_t key = key_of(MOE_MODE_INDEXED, T, topk, ovr);
+  std::lock_guard<std::mutex> g(h->mu);
+  auto it = h->cache.find(key);
+  if (it != h->cache.end()) return it->second;
+  Schedule s;
+  const int E = h->desc.num_experts;
+  const long rows = ((long)T * topk + E - 1) / E;
+  s.rows = (int)rows;
+  s.kind = rows < kLargeMRows ? SCHED_SMALL_M : SCHED_LARGE_M;
+  if (h->env.schedule) s.kind = h->env.schedule;
+  if (ovr && ovr->schedule) s.kind = ovr->schedule;
+  // The large-M kernel is not built yet: every indexed call runs small-M with
+  // tiles covering the expected rows.
+  s.kind = SCHED_SMALL_M;
+  s.nt = nt_for_rows((int)rows);
+  if (h->env.nt) s.nt = h->env.nt;
+  s.block = 16;
+  if (ovr && ovr->block_m) s.block = ovr->block_m;
+  if (h->env.log)
+    std::fprintf(stderr, "[moe_w4a16] indexed T=%d topk=%d rows/expert=%ld -> small-M nt=%d block=%d\n",
+                 T, topk, rows, s.nt, s.block);
+  h->cache.emplace(key, s);
+  return s;
+}
+
+Schedule schedule_masked(moe_weights* h, int max_m, int expected_m) {
+  const uint64_t key = key_of(MOE_MODE_MASKED, max_m, expected_m, nullptr);
+  std::lock_guard<std::mutex> g(h->mu);
+  auto it = h->cache.find(key);
+  if (it != h->cache.end()) return it->second;
+  Schedule s;
+  s.rows = expected_m;
+  // The row budget bounds every expert's rows: cover it in one weight pass
+  // when it fits four token tiles.
+  s.nt = nt_for_rows(max_m < 64 ? max_m : 64);
+  if (h->env.nt) s.nt = h->env.nt;
+  if (h->env.log)
+    std::fprintf(stderr, "[moe_w4a16] masked max_m=%d expected_m=%d -> small-M nt=%d\n", max_m,
+                 expected_m, s.nt);
+  h->cache.emplace(key, s);
+  return s;
+}
+
+Schedule schedule_contiguous(moe_weights* h, int M_pad) {
+  const uint64_t key = key_of(MOE_MODE_CONTIGUOUS, M_pad, 0, nullptr);
+  std::lock_guard<std::mutex> g(h->mu);
+  auto it = h->cache.find(key);
+  if (it != h->cache.end()) return it->second;
+  Schedule s;
+  s.rows = 128;
+  s.nt = 2;
+  if (h->env.nt) s.nt = h->env.nt;
+  h->cache.emplace(key, s);
+  return s;
+}
+
+moe_status_t check_desc(const moe_weight_desc_t* d) {
+  if (!d) return fail(MOE_ERR_INVALID_ARG, "desc is NULL");
+  if (d->bits != 4 || d->group_size != 32 || d->zero_point != 8 || d->scale_dtype != MOE_SCALE_BF16 ||
+      d->pack_order != MOE_PACK_INT32_LOW_NIBBLE_FIRST_K)
+    return fail(MOE_ERR_UNSUPPORTED_SCHEMA,
+                "unsupported quantisation schema (bits=%d group=%d zero_point=%d scale=%d pack=%d); "
+                "supported: uint4, group 32, zero point 8, BF16 scales, int32 low-nibble-first along K",
+                d->bits, d->group_size, d->zero_point, d->scale_dtype, d->pack_order);
+  if (d->hidden <= 0 || d->inter <= 0 || d->hidden % 32 || d->inter % 32)
+    return fail(MOE_ERR_UNSUPPORTED_SCHEMA, "hidden (%d) and inter (%d) must be positive multiples of 32",
+                d->hidden, d->inter);
+  if (d->hidden > (1 << 16) || d->inter > (1 << 16))
+    return fail(MOE_ERR_INVALID_ARG, "hidden/inter above 65536");
+  if (d->num_experts < 1 || d->num_experts > 4096)
+    return fail(MOE_ERR_INVALID_ARG, "num_experts %d outside 1..4096", d->num_experts);
+  if (d->mode < MOE_MODE_INDEXED || d->mode > MOE_MODE_MASKED)
+    return fail(MOE_ERR_INVALID_ARG, "unknown mode %d", d->mode);
+  return MOE_OK;
+}
+
+const char* mode_name(int m) {
+  return m == MOE_MODE_INDEXED ? "indexed" : m == MOE_MODE_CONTIGUOUS ? "contiguous" : "masked";
+}
+
+moe_status_t check_handle(const moe_weights_t* h, int mode) {
+  if (!h) return fail(MOE_ERR_INVALID_ARG, "weights handle is NULL");
+  if (h->desc.mode != mode)
+    return fail(MOE_ERR_MODE_MISMATCH, "weights were prepared for the %s layout, not %s",
+                mode_name(h->desc.mode), mode_name(mode));
+  return MOE_OK;
+}
+
+moe_status_t check_topk(const moe_weights_t* h, int T, int topk) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %d < 0", T);
+  if (topk < 1 || topk > h->desc.num_experts || topk > 64)
+    return fail(MOE_ERR_INVALID_ARG, "topk = %d outside 1..min(E, 64)", topk);
+  if ((int64_t)T * topk > (1 << 28)) return fail(MOE_ERR_INVALID_ARG, "T*topk too large");
+  return MOE_OK;
+}
+
+// Workspace carving.
+struct WsLayout {
+  size_t off_a = 0, off_acc = 0, off_routing = 0, total = 0;
+};
+
+WsLayout ws_indexed(const moe_weights_t* h, int T, int topk, int block) {
+  RoutingLayout R;
+  R.init(h->desc.num_experts, T, topk, block);
+  WsLayout w;
+  size_t o = 0;
+  w.off_a = o;
+  o = round_up(o + (size_t)R.cap * h->desc.inter * 2, kAlign);
+  w.off_acc = o;
+  o = round_up(o + (size_t)T * h->desc.hidden * 4, kAlign);
+  w.off_routing = o;
+  o = round_up(o + (size_t)R.total_ints * 4, kAlign);
+  w.total = o;
+  return w;
+}
+
+WsLayout ws_rows(const moe_weights_t* h, int64_t rows, int64_t acc_tokens) {
+  WsLayout w;
+  size_t o = 0;
+  w.off_a = o;
+  o = round_up(o + (size_t)rows * h->desc.inter * 2, kAlign);
+  w.off_acc = o;
+  o = round_up(o + (size_t)acc_tokens * h->desc.hidden * 4, kAlign);
+  w.total = o;
+  return w;
+}
+
+void fill_weights(GemmParams& p, const moe_weights_t* h, const MatLayout& m) {
+  p.wq = h->prepared + m.off_words;
+  p.wsc = h->prepared + m.off_scales;
+  p.E = m.E;
+  p.RG = m.RG;
+  p.Kc = m.Kc;
+  p.K = m.K;
+  p.N = m.N;
+  p.wg_per_set = (m.RG + 3) / 4;
+}
+
+moe_status_t set_device(const moe_weights_t* h) {
+  if (!h->prepared)
+    return fail(MOE_ERR_INVALID_ARG, "handle from moe_plan_create has no prepared weights");
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (cur != h->device) {
+    e = hipSetDevice(h->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+// --------------------------------------------------------------------------
+// ABI
+// --------------------------------------------------------------------------
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_W4A16_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+const char* moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED_SCHEMA: return "MOE_ERR_UNSUPPORTED_SCHEMA";
+    case MOE_ERR_MODE_MISMATCH: return "MOE_ERR_MODE_MISMATCH";
+    case MOE_ERR_OVERRIDE_REJECTED: return "MOE_ERR_OVERRIDE_REJECTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_ROUTING_MISMATCH: return "MOE_ERR_ROUTING_MISMATCH";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+size_t moe_prepared_bytes(const moe_weight_desc_t* desc) {
+  if (check_desc(desc) != MOE_OK) return 0;
+  PreparedLayout L;
+  L.init(desc->num_experts, desc->hidden, desc->inter);
+  g_err.clear();
+  return L.total + kAlign;   // + one status word for the load-time scale check
+}
+
+moe_status_t moe_prepare_weights(const moe_weight_desc_t* desc, const int32_t* w13_q,
+                                 const uint16_t* w13_s, const int32_t* w2_q, const uint16_t* w2_s,
+                                 void* prepared, size_t prepared_bytes, moe_stream_t stream,
+                                 moe_weights_t** out) {
+  moe_status_t st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!w13_q || !w13_s || !w2_q || !w2_s || !prepared)
+    return fail(MOE_ERR_INVALID_ARG, "a weight or prepared pointer is NULL");
+  if (!aligned(w13_q, 16) || !aligned(w2_q, 16) || !aligned(w13_s, 2) || !aligned(w2_s, 2))
+    return fail(MOE_ERR_INVALID_ARG, "packed words need 16-byte and scales 2-byte alignment");
+  if (!aligned(prepared, kAlign)) return fail(MOE_ERR_INVALID_ARG, "prepared buffer not 256-byte aligned");
+  PreparedLayout L;
+  L.init(desc->num_experts, desc->hidden, desc->inter);
+  if (prepared_bytes < L.total + kAlign)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "prepared buffer %zu bytes < %zu", prepared_bytes,
+                L.total + kAlign);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)prepared;
+  int32_t* flag = (int32_t*)(base + L.total);
+  e = run("zero_flag", s, [&] { return launch_zero_i32(flag, 1, s); });
+  if (e == hipSuccess)
+    e = run("repack_w13", s, [&] { return launch_repack(L.w13, w13_q, w13_s, base, flag, s); });
+  if (e == hipSuccess)
+    e = run("repack_w2", s, [&] { return launch_repack(L.w2, w2_q, w2_s, base, flag, s); });
+  if (e != hipSuccess) return hip_fail(e, "repack launch");
+  int32_t bad = 0;
+  e = hipMemcpyAsync(&bad, flag, sizeof bad, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "prepare synchronise");
+  if (bad)
+    return fail(MOE_ERR_UNSUPPORTED_SCHEMA,
+                "a scale is NaN, infinite or of magnitude >= 2^125 (outside the supported range)");
+  moe_weights* h = new moe_weights();
+  h->desc = *desc;
+  h->lay = L;
+  h->prepared = base;
+  h->prepared_bytes = prepared_bytes;
+  h->device = dev;
+  h->env.read();
+  *out = h;
+  return ok();
+}
+
+void moe_release_weights(moe_weights_t* h) { delete h; }
+
+moe_weights_t* moe_plan_create(const moe_weight_desc_t* desc) {
+  if (check_desc(desc) != MOE_OK) return nullptr;
+  moe_weights* h = new moe_weights();
+  h->desc = *desc;
+  h->lay.init(desc->num_experts, desc->hidden, desc->inter);
+  h->prepared = nullptr;
+  h->device = -1;
+  h->env.read();
+  g_err.clear();
+  return h;
+}
+
+int32_t moe_routing_block(const moe_weights_t* h, int32_t T, int32_t topk, const moe_tuning_t* ovr) {
+  if (check_handle(h, MOE_MODE_INDEXED) != MOE_OK || check_topk(h, T, topk) != MOE_OK) return 0;
+  if (ovr && ovr->block_m && ovr->block_m != 16 && ovr->block_m != 32 && ovr->block_m != 64 &&
+      ovr->block_m != 128) {
+    fail(MOE_ERR_INVALID_ARG, "block_m %d not in {16, 32, 64, 128}", ovr->block_m);
+    return 0;
+  }
+  g_err.clear();
+  return schedule_indexed(const_cast<moe_weights_t*>(h), T, topk, ovr).block;
+}
+
+moe_status_t moe_routing_layout(const moe_weights_t* h, int32_t T, int32_t topk,
+                                const moe_tuning_t* ovr, moe_routing_layout_t* out) {
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  const int B = moe_routing_block(h, T, topk, ovr);
+  if (!B) return h ? (h->desc.mode != MOE_MODE_INDEXED ? MOE_ERR_MODE_MISMATCH : MOE_ERR_INVALID_ARG)
+                   : MOE_ERR_INVALID_ARG;
+  RoutingLayout R;
+  R.init(h->desc.num_experts, T, topk, B);
+  out->block = R.block;
+  out->cap = R.cap;
+  out->nblocks = R.nblocks;
+  out->sentinel = R.sentinel;
+  out->off_header = R.off_header;
+  out->off_counts = R.off_counts;
+  out->off_offsets = R.off_offsets;
+  out->off_sorted = R.off_sorted;
+  out->off_block_expert = R.off_block_expert;
+  out->off_scratch = R.off_scratch;
+  out->total_ints = R.total_ints;
+  return ok();
+}
+
+size_t moe_routing_bytes(const moe_weights_t* h, int32_t T, int32_t topk, const moe_tuning_t* ovr) {
+  moe_routing_layout_t L;
+  if (moe_routing_layout(h, T, topk, ovr, &L) != MOE_OK) return 0;
+  return (size_t)L.total_ints * 4;
+}
+
+moe_status_t moe_align(const moe_weights_t* h, const int32_t* topk_ids, int32_t T, int32_t topk,
+                       const moe_tuning_t* ovr, void* routing, size_t routing_bytes,
+                       moe_stream_t stream) {
+  moe_status_t st = check_handle(h, MOE_MODE_INDEXED);
+  if (st != MOE_OK) return st;
+  if ((st = check_topk(h, T, topk)) != MOE_OK) return st;
+  if (!routing || (T > 0 && !topk_ids)) return fail(MOE_ERR_INVALID_ARG, "NULL routing or topk_ids");
+  if (!aligned(routing, 4) || (topk_ids && !aligned(topk_ids, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "routing / topk_ids not 4-byte aligned");
+  const int B = moe_routing_block(h, T, topk, ovr);
+  if (!B) return MOE_ERR_INVALID_ARG;
+  RoutingLayout R;
+  R.init(h->desc.num_experts, T, topk, B);
+  if (routing_bytes < (size_t)R.total_ints * 4)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "routing buffer %zu bytes < %zu", routing_bytes,
+                (size_t)R.total_ints * 4);
+  if ((st = set_device(h)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = run("align", s, [&] {
+    return launch_align(topk_ids, T, topk, h->desc.num_experts, R, (int32_t*)routing, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "align launch");
+  return ok();
+}
+
+moe_status_t moe_permute(const moe_weights_t* h, const uint16_t* x, int32_t T, int32_t topk,
+                         const moe_tuning_t* ovr, const void* routing, uint16_t* a_out,
+                         int32_t* m_indices, int32_t* row_src, moe_stream_t stream) {
+  moe_status_t st = check_handle(h, MOE_MODE_INDEXED);
+  if (st != MOE_OK) return st;
+  if ((st = check_topk(h, T, topk)) != MOE_OK) return st;
+  if (!routing) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
+  if (a_out && T > 0 && !x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
+  if ((a_out && !aligned(a_out, 16)) || (x && !aligned(x, 16)))
+    return fail(MOE_ERR_INVALID_ARG, "x / a_out not 16-byte aligned");
+  const int B = moe_routing_block(h, T, topk, ovr);
+  if (!B) return MOE_ERR_INVALID_ARG;
+  RoutingLayout R;
+  R.init(h->desc.num_experts, T, topk, B);
+  if ((st = set_device(h)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = run("permute", s, [&] {
+    return launch_permute(x, T, topk, h->desc.hidden, R, (const int32_t*)routing, a_out, m_indices,
+                          row_src, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "permute launch");
+  return ok();
+}
+
+size_t moe_workspace_bytes(const moe_weights_t* h, int32_t mode, int32_t rows, int32_t topk,
+                           int32_t tokens, const moe_tuning_t* ovr) {
+  if (check_handle(h, mode) != MOE_OK) return 0;
+  if (mode == MOE_MODE_INDEXED) {
+    const int B = moe_routing_block(h, rows, topk, ovr);
+    if (!B) return 0;
+    return ws_indexed(h, rows, topk, B).total;
+  }
+  if (rows < 0 || tokens < 0) {
+    fail(MOE_ERR_INVALID_ARG, "negative rows / tokens");
+    return 0;
+  }
+  g_err.clear();
+  if (mode == MOE_MODE_MASKED) return ws_rows(h, (int64_t)h->desc.num_experts * rows, 0).total;
+  return ws_rows(h, rows, topk > 0 ? tokens : 0).total;
+}
+
+moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32_t T, int32_t topk,
+                               const int32_t* topk_ids, const float* topk_w, const void* routing,
+                               uint16_t* out, void* ws, size_t ws_bytes, const moe_tuning_t* ovr,
+                               moe_stream_t stream) {
+  moe_weights_t* h = const_cast<moe_weights_t*>(hc);
+  moe_status_t st = check_handle(h, MOE_MODE_INDEXED);
+  if (st != MOE_OK) return st;
+  if ((st = check_topk(h, T, topk)) != MOE_OK) return st;
+  if (ovr && ovr->schedule && (ovr->schedule < 0 || ovr->schedule > 2))
+    return fail(MOE_ERR_INVALID_ARG, "schedule override %d not in 0..2", ovr->schedule);
+  const int B = moe_routing_block(h, T, topk, ovr);
+  if (!B) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return ok();
+  if (!x || !topk_w || !out || !ws || (!routing && !topk_ids))
+    return fail(MOE_ERR_INVALID_ARG, "NULL x / topk_w / out / ws / topk_ids");
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, kAlign) || !aligned(topk_w, 4) ||
+      (routing && !aligned(routing, 4)) || (topk_ids && !aligned(topk_ids, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "misaligned pointer (x/out 16 B, ws 256 B, others 4 B)");
+  const Schedule sc = schedule_indexed(h, T, topk, ovr);
+  const WsLayout W = ws_indexed(h, T, topk, B);
+  const size_t need = routing ? W.off_routing : W.total;
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu", ws_bytes, need);
+  if ((st = set_device(h)) != MOE_OK) return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  RoutingLayout R;
+  R.init(h->desc.num_experts, T, topk, B);
+  const int32_t* rt = (const int32_t*)routing;
+  hipError_t e = hipSuccess;
+  if (!rt) {
+    int32_t* own = (int32_t*)(wsb + W.off_routing);
+    e = run("align", s, [&] { return launch_align(topk_ids, T, topk, h->desc.num_experts, R, own, s); });
+    rt = own;
+  }
+  const int H = h->desc.hidden, I = h->desc.inter, E = h->desc.num_experts;
+  uint16_t* a_ws = (uint16_t*)(wsb + W.off_a);
+  float* acc = (float*)(wsb + W.off_acc);
+  if (e == hipSuccess) e = run("zero_acc", s, [&] { return launch_zero_f32(acc, (size_t)T * H, s); });
+
+  GemmParams p{};
+  p.counts = rt + R.off_counts;
+  p.offsets = rt + R.off_offsets;
+  p.sorted_ids = rt + R.off_sorted;
+  p.routing_hdr = rt;
+  p.sentinel = T * topk;
+  p.topk = topk;
+  p.block = B;
+  p.nsets = E;
+
+  GemmParams p13 = p;
+  fill_weights(p13, h, h->lay.w13);
+  p13.total_wg = E * p13.wg_per_set;
+  p13.src = x;
+  p13.src_ld = H;
+  p13.gather = 1;
+  p13.a_out = a_ws;
+  p13.a_ld = I;
+  if (e == hipSuccess)
+    e = run("gemm_w13_small_m", s, [&] { return launch_gemm_small_m(p13, SET_INDEXED, EPI_SWIGLU, sc.nt, s); });
+
+  GemmParams p2 = p;
+  fill_weights(p2, h, h->lay.w2);
+  p2.total_wg = E * p2.wg_per_set;
+  p2.src = a_ws;
+  p2.src_ld = I;
+  p2.acc_out = acc;
+  p2.topk_w = topk_w;
+  p2.acc_ld = H;
+  if (e == hipSuccess)
+    e = run("gemm_w2_small_m", s, [&] { return launch_gemm_small_m(p2, SET_INDEXED, EPI_COMBINE, sc.nt, s); });
+  if (e == hipSuccess)
+    e = run("combine_to_bf16", s, [&] { return launch_f32_to_bf16(acc, out, (size_t)T * H, s); });
+  if (e != hipSuccess) return hip_fail(e, "indexed launch");
+  return ok();
+}
+
+moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, int32_t M_pad,
+                                  const int32_t* m_indices, const int32_t* row_src,
+                                  const float* topk_w, int32_t T, int32_t topk, uint16_t* out,
+                                  void* ws, size_t ws_bytes, const moe_tuning_t* ovr,
+                                  moe_stream_t stream) {
+  moe_weights_t* h = const_cast<moe_weights_t*>(hc);
+  moe_status_t st = check_handle(h, MOE_MODE_CONTIGUOUS);
+  if (st != MOE_OK) return st;
+  if (ovr)
+    return fail(MOE_ERR_OVERRIDE_REJECTED,
+                "the contiguous layout chooses its own schedule; tuning overrides are indexed-only");
+  if (M_pad < 0 || M_pad % 128)
+    return fail(MOE_ERR_INVALID_ARG, "M_pad = %d must be a non-negative multiple of 128", M_pad);
+  if (row_src && (st = check_topk(h, T, topk)) != MOE_OK) return st;
+  if (M_pad == 0) return ok();
+  if (!a || !m_indices || !out || !ws || (row_src && !topk_w))
+    return fail(MOE_ERR_INVALID_ARG, "NULL a / m_indices / out / ws / topk_w");
+  if (!aligned(a, 16) || !aligned(out, 16) || !aligned(ws, kAlign) || !aligned(m_indices, 4) ||
+      (row_src && (!aligned(row_src, 4) || !aligned(topk_w, 4))))
+    return fail(MOE_ERR_INVALID_ARG, "misaligned pointer (a/out 16 B, ws 256 B, others 4 B)");
+  const WsLayout W = ws_rows(h, M_pad, row_src ? T : 0);
+  if (ws_bytes < W.total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu", ws_bytes, W.total);
+  if ((st = set_device(h)) != MOE_OK) return st;
+  const Schedule sc = schedule_contiguous(h, M_pad);
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  const int H = h->desc.hidden, I = h->desc.inter;
+  uint16_t* a_ws = (uint16_t*)(wsb + W.off_a);
+  float* acc = (float*)(wsb + W.off_acc);
+  hipError_t e = hipSuccess;
+  if (row_src && T > 0) e = run("zero_acc", s, [&] { return launch_zero_f32(acc, (size_t)T * H, s); });
+
+  GemmParams p{};
+  p.m_indices = m_indices;
+  p.row_src = row_src;
+  p.block_rows = 128;
+  p.nsets = M_pad / 128;
+  p.sentinel = row_src ? T * topk : 0;
+  p.topk = row_src ? topk : 1;
+
+  GemmParams p13 = p;
+  fill_weights(p13, h, h->lay.w13);
+  p13.total_wg = p13.nsets * p13.wg_per_set;
+  p13.src = a;
+  p13.src_ld = H;
+  p13.a_out = a_ws;
+  p13.a_ld = I;
+  if (e == hipSuccess)
+    e = run("gemm_w13_small_m", s, [&] { return launch_gemm_small_m(p13, SET_BLOCKS, EPI_SWIGLU, sc.nt, s); });
+
+  GemmParams p2 = p;
+  fill_weights(p2, h, h->lay.w2);
+  p2.total_wg = p2.nsets * p2.wg_per_set;
+  p2.src = a_ws;
+  p2.src_ld = I;
+  if (row_src) {
+    p2.acc_out = acc;
+    p2.topk_w = topk_w;
+    p2.acc_ld = H;
+    if (e == hipSuccess)
+      e = run("gemm_w2_small_m", s, [&] { return launch_gemm_small_m(p2, SET_BLOCKS, EPI_COMBINE, sc.nt, s); });
+    if (e == hipSuccess && T > 0)
+      e = run("combine_to_bf16", s, [&] { return launch_f32_to_bf16(acc, out, (size_t)T * H, s); });
+  } else {
+    p2.out = out;
+    p2.out_ld = H;
+    if (e == hipSuccess)
+      e = run("gemm_w2_small_m", s, [&] { return launch_gemm_small_m(p2, SET_BLOCKS, EPI_STORE, sc.nt, s); });
+  }
+  if (e != hipSuccess) return hip_fail(e, "contiguous launch");
+  return ok();
+}
+
+moe_status_t moe_w4a16_masked(const moe_weights_t* hc, const uint16_t* a3, int32_t max_m,
+                              const int32_t* masked_m, int32_t expected_m, uint16_t* out, void* ws,
+                              size_t ws_bytes, const moe_tuning_t* ovr, moe_stream_t stream) {
+  moe_weights_t* h = const_cast<moe_weights_t*>(hc);
+  moe_status_t st = check_handle(h, MOE_MODE_MASKED);
+  if (st != MOE_OK) return st;
+  if (ovr)
+    return fail(MOE_ERR_OVERRIDE_REJECTED,
+                "the masked layout chooses its own schedule; tuning overrides are indexed-only");
+  if (expected_m <= 0) return fail(MOE_ERR_INVALID_ARG, "expected_m = %d must be positive", expected_m);
+  if (max_m < 0 || (int64_t)max_m * h->desc.num_experts > (1 << 28))
+    return fail(MOE_ERR_INVALID_ARG, "max_m = %d out of range", max_m);
+  if (max_m == 0) return ok();
+  if (!a3 || !masked_m || !out || !ws) return fail(MOE_ERR_INVALID_ARG, "NULL a3 / masked_m / out / ws");
+  if (!aligned(a3, 16) || !aligned(out, 16) || !aligned(ws, kAlign) || !aligned(masked_m, 4))
+    return fail(MOE_ERR_INVALID_ARG, "misaligned pointer (a3/out 16 B, ws 256 B, masked_m 4 B)");
+  const WsLayout W = ws_rows(h, (int64_t)h->desc.num_experts * max_m, 0);
+  if (ws_bytes < W.total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu", ws_bytes, W.total);
+  if ((st = set_device(h)) != MOE_OK) return st;
+  const Schedule sc = schedule_masked(h, max_m, expected_m);
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  const int H = h->desc.hidden, I = h->desc.inter, E = h->desc.num_experts;
+  uint16_t* a_ws = (uint16_t*)(wsb + W.off_a);
+  GemmParams p{};
+  p.masked_m = masked_m;
+  p.max_m = max_m;
+  p.nsets = E;
+  p.topk = 1;
+
+  GemmParams p13 = p;
+  fill_weights(p13, h, h->lay.w13);
+  p13.total_wg = E * p13.wg_per_set;
+  p13.src = a3;
+  p13.src_ld = H;
+  p13.a_out = a_ws;
+  p13.a_ld = I;
+  hipError_t e = run("gemm_w13_small_m", s, [&] { return launch_gemm_small_m(p13, SET_MASKED, EPI_SWIGLU, sc.nt, s); });
+
+  GemmParams p2 = p;
+  fill_weights(p2, h, h->lay.w2);
+  p2.total_wg = E * p2.wg_per_set;
+  p2.src = a_ws;
+  p2.src_ld = I;
+  p2.out = out;
+  p2.out_ld = H;
+  if (e == hipSuccess)
+    e = run("gemm_w2_small_m", s, [&] { return launch_gemm_small_m(p2, SET_MASKED, EPI_STORE, sc.nt, s); });
+  if (e != hipSuccess) return hip_fail(e, "masked launch");
+  return ok();
+}
+
+moe_status_t moe_dequant_weights(const moe_weights_t* h, int32_t which, int32_t expert,
+                                 uint16_t* out, moe_stream_t stream) {
+  if (!h) return fail(MOE_ERR_INVALID_ARG, "weights handle is NULL");
+  if (which != 13 && which != 2) return fail(MOE_ERR_INVALID_ARG, "which = %d must be 13 or 2", which);
+  if (expert < 0 || expert >= h->desc.num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "expert %d outside 0..%d", expert, h->desc.num_experts - 1);
+  if (!out || !aligned(out, 16)) return fail(MOE_ERR_INVALID_ARG, "out NULL or not 16-byte aligned");
+  moe_status_t st = set_device(h);
+  if (st != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const MatLayout& m = which == 13 ? h->lay.w13 : h->lay.w2;
+  hipError_t e = run("dequant_expert", s, [&] { return launch_dequant_expert(m, h->prepared, expert, out, s); });
+  if (e != hipSuccess) return hip_fail(e, "dequant launch");
+  return ok();
+}
+
+int moe_describe(const moe_weights_t* hc, int32_t mode, int32_t rows, int32_t topk,
+                 int32_t expected_m, const moe_tuning_t* ovr, char* buf, size_t n) {
+  moe_weights_t* h = const_cast<moe_weights_t*>(hc);
+  if (!buf || n == 0 || check_handle(h, mode) != MOE_OK) return -1;
+  const int E = h->desc.num_experts;
+  const int wg13 = (h->lay.w13.RG + 3) / 4, wg2 = (h->lay.w2.RG + 3) / 4;
+  int len = -1;
+  if (mode == MOE_MODE_INDEXED) {
+    if (check_topk(h, rows, topk) != MOE_OK) return -1;
+    const Schedule s = schedule_indexed(h, rows, topk, ovr);
+    len = std::snprintf(buf, n,
+                        "layout=indexed T=%d topk=%d rows_per_expert=%d schedule=small-M block=%d nt=%d "
+                        "grid_w13=%d grid_w2=%d",
+                        rows, topk, s.rows, s.block, s.nt, E * wg13, E * wg2);
+  } else if (mode == MOE_MODE_MASKED) {
+    if (expected_m <= 0 || rows < 0) return -1;
+    const Schedule s = schedule_masked(h, rows, expected_m);
+    len = std::snprintf(buf, n,
+                        "layout=masked max_m=%d expected_m=%d schedule=small-M nt=%d grid_w13=%d grid_w2=%d",
+                        rows, expected_m, s.nt, E * wg13, E * wg2);
+  } else {
+    if (rows < 0 || rows % 128) return -1;
+    const Schedule s = schedule_contiguous(h, rows);
+    len = std::snprintf(buf, n,
+                        "layout=contiguous M_pad=%d blocks=%d schedule=small-M nt=%d grid_w13=%d grid_w2=%d",
+                        rows, rows / 128, s.nt, (rows / 128) * wg13, (rows / 128) * wg2);
+  }
+  if (len < 0) return -1;
+  return len < (int)n ? len : (int)n - 1;
+}
+
+moe_status_t moe_profile_enable(int enable) {
+  Profiler& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  P.on = enable != 0;
+  return ok();
+}
+
+void moe_profile_reset(void) {
+  Profiler& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  P.drain();
+  P.totals.clear();
+}
+
+int moe_profile_read(char* buf, size_t n) {
+  if (!buf || n == 0) return -1;
+  Profiler& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  P.drain();
+  std::string s;
+  char line[256];
+  for (auto& kv : P.totals) {
+    std::snprintf(line, sizeof line, "%s %ld %.6f\n", kv.first.c_str(), kv.second.first, kv.second.second);
+    s += line;
+  }
+  const size_t m = s.size() < n - 1 ? s.size() : n - 1;
+  std::memcpy(buf, s.data(), m);
+  buf[m] = 0;
+  return (int)m;
+}
+
+}  // extern "C"

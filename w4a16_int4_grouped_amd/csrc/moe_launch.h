@@ -1,0 +1,73 @@
+// Kernel launchers (host side). Each returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_layout.h"
+
+namespace moe {
+
+// How the rows of one work item are found.
+enum RowSet : int {
+  SET_INDEXED = 0,   // expert e: slots offsets[e] .. + counts[e]
+  SET_MASKED = 1,    // expert e: slots e*max_m .. + clamp(masked_m[e])
+  SET_BLOCKS = 2,    // block b of block_rows slots; expert from m_indices
+};
+
+// What the GEMM does with its FP32 tile.
+enum Epilogue : int {
+  EPI_SWIGLU = 0,    // W13: a[slot][c] = bf16(silu(gate) * up)
+  EPI_COMBINE = 1,   // W2: acc[t][n] += w[f] * y   (f from sorted_ids / row_src)
+  EPI_STORE = 2,     // W2: out[slot][n] = bf16(y)
+};
+
+struct GemmParams {
+  // prepared weights of one matrix
+  const void* wq;        // u32x4 [E][RG][Kc][4][64]
+  const void* wsc;       // u16 [E][RG][Kc][64][4]
+  int E, RG, Kc, K, N;   // N: true rows (output features)
+  int wg_per_set;        // workgroups per row set = ceil(RG / 4)
+  int nsets;             // row sets (experts or blocks)
+  int total_wg;
+  // row sets
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* sorted_ids;
+  const int32_t* routing_hdr;
+  int sentinel, topk, block;  // indexed
+  const int32_t* masked_m;
+  int max_m;                  // masked
+  const int32_t* m_indices;
+  int block_rows;             // blocks (contiguous)
+  const int32_t* row_src;     // blocks with combine
+  // B operand rows
+  const uint16_t* src;
+  int64_t src_ld;             // elements per row
+  int gather;                 // 1: row = sorted_ids[slot] / topk
+  // epilogue targets
+  uint16_t* a_out;
+  int64_t a_ld;               // SWIGLU
+  float* acc_out;
+  const float* topk_w;
+  int64_t acc_ld;             // COMBINE
+  uint16_t* out;
+  int64_t out_ld;             // STORE
+};
+
+hipError_t launch_gemm_small_m(const GemmParams& p, int set, int epi, int nt, hipStream_t s);
+
+hipError_t launch_align(const int32_t* topk_ids, int T, int topk, int E, const RoutingLayout& L,
+                        int32_t* routing, hipStream_t s);
+hipError_t launch_permute(const uint16_t* x, int T, int topk, int H, const RoutingLayout& L,
+                          const int32_t* routing, uint16_t* a_out, int32_t* m_indices,
+                          int32_t* row_src, hipStream_t s);
+hipError_t launch_repack(const MatLayout& m, const int32_t* words, const uint16_t* scales,
+                         char* prepared, int32_t* bad_scale_flag, hipStream_t s);
+hipError_t launch_dequant_expert(const MatLayout& m, const char* prepared, int expert,
+                                 uint16_t* out, hipStream_t s);
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s);
+hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t s);
+hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s);
+
+}  // namespace moe
