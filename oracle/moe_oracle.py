@@ -61,7 +61,8 @@ def bf16_round(x) -> np.ndarray:
 def bf16_to_f64(bits) -> np.ndarray:
     """BF16 bit patterns (uint16) to float64 values (exact)."""
     b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << 16
-    return b.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
 
 
 # --------------------------------------------------------------------------

@@ -68,28 +68,49 @@ def prepare(weights_np, mode="indexed", dev_weights=None):
     return M.PreparedWeights(*dw, mode=mode)
 
 
+# If rounding the reference itself to BF16 (the output dtype) already errs by
+# more than the max-abs bound, no BF16 output can meet it; the check then
+# bounds the excess over that floor instead.
+FLOOR_EXCESS_TOL = 5e-3
+
+
 def check_tol(got, ref, what=""):
-    """Layer-output parity: relFro <= 5e-3 and max-abs <= 3e-2 * rms(ref)."""
+    """Layer-output parity: relFro <= 5e-3 and max-abs <= 3e-2 * rms(ref)
+    (or <= floor + 5e-3 * rms(ref) when the BF16 output floor exceeds
+    3e-2 * rms(ref))."""
     from oracle import compare
     m = compare(got, ref)
+    bound = MAX_ABS_TOL if m["bf16_floor"] <= MAX_ABS_TOL else m["bf16_floor"] + FLOOR_EXCESS_TOL
     log(f"  parity {what}: rel_fro={m['rel_fro']:.3e} max_abs/rms={m['max_abs_over_rms']:.3e} "
-        f"bf16_floor={m['bf16_floor']:.3e} n={m['n']}")
+        f"bf16_floor={m['bf16_floor']:.3e} bound={bound:.3e} n={m['n']}")
     assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
     assert m["rel_fro"] <= REL_FRO_TOL, (what, m)
-    assert m["max_abs_over_rms"] <= MAX_ABS_TOL, (what, m)
+    assert m["max_abs_over_rms"] <= bound, (what, m)
     return m
 
 
 def a_mismatch(got_bits: np.ndarray, ref_bits: np.ndarray, what=""):
-    """Intermediate `a` (BF16): fraction of elements that differ and the
-    largest difference in units of the last place."""
+    """Intermediate `a` (BF16, the second GEMM's input): fraction of elements
+    that differ, the largest difference in ulps, and whether every difference
+    is within one ulp of the reference value plus 2^-8 * rms(a).
+
+    The GPU accumulates h in FP32, the oracle in float64, so a differs in
+    rare elements: a 1-ulp flip where silu(g)*u sits near a rounding
+    boundary, or a few ulps of a small value when h suffers cancellation
+    (the DFlash audit's point, section 2: a segmented BF16/FP32
+    accumulation changes rounding, so intermediates are compared)."""
+    from oracle import moe_oracle as O
     g = got_bits.astype(np.int32)
     r = ref_bits.astype(np.int32)
-    # order-preserving integer view of bf16
+
     def ordered(v):
         return np.where(v & 0x8000, 0x8000 - (v & 0x7FFF), 0x8000 + v)
     diff = np.abs(ordered(g) - ordered(r))
     frac = float(np.mean(diff != 0)) if diff.size else 0.0
     mx = int(diff.max()) if diff.size else 0
-    log(f"  intermediate a {what}: mismatch fraction {frac:.2e}, max ulp {mx}")
-    return frac, mx
+    gv, rv = O.bf16_to_f64(got_bits), O.bf16_to_f64(ref_bits)
+    rms = float(np.sqrt(np.mean(rv ** 2))) if rv.size else 0.0
+    ulp = np.ldexp(1.0, np.frexp(np.abs(rv))[1] - 8)
+    within = bool(np.all(np.abs(gv - rv) <= ulp + 2.0 ** -8 * rms))
+    log(f"  intermediate a {what}: mismatch fraction {frac:.2e}, max ulp {mx}, within bound {within}")
+    return frac, mx, within

@@ -415,7 +415,7 @@ moe_status_t moe_prepare_weights(const moe_weight_desc_t* desc, const int32_t* w
   if (e != hipSuccess) return hip_fail(e, "prepare synchronise");
   if (bad)
     return fail(MOE_ERR_UNSUPPORTED_SCHEMA,
-                "a scale is NaN, infinite or of magnitude >= 2^125 (outside the supported range)");
+                "a scale is NaN, infinite or of magnitude >= 2^124 (outside the supported range)");
   moe_weights* h = new moe_weights();
   h->desc = *desc;
   h->lay = L;

@@ -26,34 +26,41 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Dequantise one packed word: eight uint4 values, low nibble first along K,
-// with zero point 8 and scale s (Chord page, "H200 and Blackwell indexed
-// decode": subtract-then-scale fused into the nibble extraction, keeping the
-// unfused BF16 rounding order).
+// v_cvt_off_f32_i4 on byte n of v (SDWA operand select): bits [3:0] of that
+// byte, read as a signed 4-bit integer i, become the float i / 16 (exact).
+#define MOE_CVT_OFF_BYTE(SEL)                                                         \
+  __device__ __forceinline__ float cvt_off_##SEL(uint32_t v) {                        \
+    float r;                                                                          \
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:" #SEL \
+        : "=v"(r)                                                                     \
+        : "v"(v));                                                                    \
+    return r;                                                                         \
+  }
+MOE_CVT_OFF_BYTE(BYTE_0)
+MOE_CVT_OFF_BYTE(BYTE_1)
+MOE_CVT_OFF_BYTE(BYTE_2)
+MOE_CVT_OFF_BYTE(BYTE_3)
+#undef MOE_CVT_OFF_BYTE
+
+// Dequantise one prepared word: eight uint4 values q, low nibble first along
+// K, stored as q ^ 8 (which, read as a signed 4-bit integer, is q - 8), with
+// the group scale given as s16 = 16 * s (Chord page, "H200 and Blackwell
+// indexed decode": subtract-then-scale fused into the nibble extraction,
+// keeping the unfused BF16 rounding order).
 //
-// fma(q, s, -8s) = q*s - 8*s is computed exactly before its single rounding,
-// and the exact value (q - 8)*s has at most 4 + 8 significant bits, so the
-// FP32 result is exactly (q - 8)*s (for |s| < 2^125, which keeps -8s finite);
-// v_cvt_pk_bf16_f32 then rounds it once to BF16. The result is bit-identical
-// to bf16_rne((q - 8) * s).
-//
-// The nibbles are split into two byte-aligned words so that
-// v_cvt_f32_ubyte{0..3} reads each value directly; the empty asm hides the
-// masks from the optimiser, which would otherwise re-extract every nibble
-// with its own bit-field instruction.
+// v_cvt_off_f32_i4 gives (q - 8) / 16 exactly, the product with 16 * s is
+// exactly (q - 8) * s (at most 4 + 8 significant bits, signed zeros
+// included), and v_cvt_pk_bf16_f32 rounds it once to BF16: bit-identical to
+// bf16_rne((q - 8) * s). The low nibble of each byte is read in place; the
+// high nibbles after one 4-bit shift of the word.
 // Result dword m holds k = 2m (low half) and k = 2m+1 (high half).
-__device__ __forceinline__ u32x4_t dq8(uint32_t w, float s, float neg8s) {
-  uint32_t lo = w & 0x0F0F0F0Fu;
-  uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-  asm("" : "+v"(lo));
-  asm("" : "+v"(hi));
+__device__ __forceinline__ u32x4_t dq8(uint32_t w, float s16) {
+  const uint32_t h = w >> 4;
   u32x4_t r;
-  r[0] = pack_bf16x2(fmaf((float)(lo & 0xFFu), s, neg8s), fmaf((float)(hi & 0xFFu), s, neg8s));
-  r[1] = pack_bf16x2(fmaf((float)((lo >> 8) & 0xFFu), s, neg8s),
-                     fmaf((float)((hi >> 8) & 0xFFu), s, neg8s));
-  r[2] = pack_bf16x2(fmaf((float)((lo >> 16) & 0xFFu), s, neg8s),
-                     fmaf((float)((hi >> 16) & 0xFFu), s, neg8s));
-  r[3] = pack_bf16x2(fmaf((float)(lo >> 24), s, neg8s), fmaf((float)(hi >> 24), s, neg8s));
+  r[0] = pack_bf16x2(cvt_off_BYTE_0(w) * s16, cvt_off_BYTE_0(h) * s16);
+  r[1] = pack_bf16x2(cvt_off_BYTE_1(w) * s16, cvt_off_BYTE_1(h) * s16);
+  r[2] = pack_bf16x2(cvt_off_BYTE_2(w) * s16, cvt_off_BYTE_2(h) * s16);
+  r[3] = pack_bf16x2(cvt_off_BYTE_3(w) * s16, cvt_off_BYTE_3(h) * s16);
   return r;
 }
 

@@ -70,13 +70,12 @@ __device__ __forceinline__ void load_chunk(Frags<NT>& f, const u32x4_t* __restri
 
 template <int NT>
 __device__ __forceinline__ void mma_chunk(const Frags<NT>& f, f32x4_t (&acc)[kMT][NT]) {
-  const float s[4] = {bf16_lo(f.S[0]), bf16_hi(f.S[0]), bf16_lo(f.S[1]), bf16_hi(f.S[1])};
+  const float s16[4] = {bf16_lo(f.S[0]), bf16_hi(f.S[0]), bf16_lo(f.S[1]), bf16_hi(f.S[1])};
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) {
-    const float neg8s = -8.0f * s[mt];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const u32x4_t a = dq8(f.A[mt][g], s[mt], neg8s);
+      const u32x4_t a = dq8(f.A[mt][g], s16[mt]);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16(a, f.B[nt][g], acc[mt][nt]);
     }
