@@ -37,7 +37,26 @@ def parse():
     ap.add_argument("--workload", type=int, default=1, help="index into synth.WORKLOADS (indexed layouts)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=8, help="experts in the oracle's timed sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (steps times), the "
+                         "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def copy_calibration(mib, steps):
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_bytes": n, "ms_per_copy": ms, "GBps_read_plus_write": 2 * n / ms / 1e6}))
 
 
 def log(*a):
@@ -80,6 +99,9 @@ def cpu_baseline(wl, w, x, ids, tw, n_experts):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)

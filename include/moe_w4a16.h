@@ -130,7 +130,7 @@ size_t moe_prepared_bytes(const moe_weight_desc_t* desc);
  *             after the call returns.
  *   out    host: receives a new handle (release with moe_release_weights).
  * Synchronises `stream` once. Errors: INVALID_ARG, UNSUPPORTED_SCHEMA (also
- * when a scale is NaN, infinite or of magnitude >= 2^124, checked on the
+ * when a scale is NaN, infinite or of magnitude >= 2^117, checked on the
  * device), WORKSPACE_TOO_SMALL, HIP. */
 moe_status_t moe_prepare_weights(const moe_weight_desc_t* desc, const int32_t* w13_q,
                                  const uint16_t* w13_s, const int32_t* w2_q,

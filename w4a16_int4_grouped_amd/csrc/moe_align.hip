@@ -4,15 +4,19 @@
 // sentinels in the routing indices).
 //
 // The result must be bit-exact and deterministic, so rows are never placed
-// by atomic order. Three passes over fixed chunks of kAlignChunk flat rows:
-//   1. count:   per-chunk expert histograms (LDS atomics; counts only);
-//   2. scan:    per expert, an exclusive prefix over chunks; padded counts
-//               ceil(c/B)*B; an exclusive scan over experts -> offsets;
-//               sentinel fill of pad slots; the block -> expert map;
-//   3. scatter: one wave per chunk walks its rows in order, 64 at a time;
-//               a row's slot is offsets[e] + (rows of e in earlier chunks) +
-//               (rows of e earlier in this chunk), i.e. a stable order by
-//               flat index t*topk + j.
+// by atomic order. Rows are placed in rounds of consecutive flat indices,
+// one 64-row slice per wave; a row's slot is
+//   (next free slot of its expert before the round)
+//   + (rows of that expert in earlier waves of the round)
+//   + (rows of that expert in earlier lanes of its wave),
+// which is the stable order by flat index t*topk + j.
+//
+// Two paths:
+//   small (decode-sized routings): one workgroup of 16 waves counts, scans,
+//     fills the padding and places every row in a single launch;
+//   large: per-chunk counts, a one-workgroup scan over experts (which also
+//     turns the chunk counts into per-chunk prefixes), then one 4-wave
+//     workgroup per chunk places that chunk's rows.
 #include <hip/hip_runtime.h>
 
 #include "moe_device.h"
@@ -24,7 +28,147 @@ namespace {
 
 constexpr int kCountThreads = 256;
 constexpr int kScanThreads = 1024;
+constexpr int kSmallMaxRows = 16384;   // small path limits
+constexpr int kSmallMaxExperts = 512;
 
+// Lanes of this wave routed to the same expert as this lane (e < 0: none).
+// Loops once per distinct expert in the wave.
+__device__ __forceinline__ uint64_t match_peers(int e) {
+  uint64_t todo = __ballot(e >= 0);
+  uint64_t peers = 0;
+  while (todo) {
+    const int j = __ffsll((unsigned long long)todo) - 1;
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    const uint64_t m = __ballot(e == ej);
+    if (e == ej) peers = m;
+    todo &= ~m;
+  }
+  return peers;
+}
+
+// Places flat rows [lo, hi) stably. next[e] (LDS) holds expert e's next free
+// slot and is advanced; cnt (LDS, NWAVES x E) must be zero on entry and is
+// zero on exit. Called by all NWAVES*64 threads of the workgroup.
+template <int NWAVES>
+__device__ void place_rows(const int32_t* __restrict__ ids, int lo, int hi, int E,
+                           int32_t* next, int32_t* cnt, int32_t* __restrict__ sorted_ids) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  for (int r0 = lo; r0 < hi; r0 += NWAVES * 64) {
+    const int f = r0 + (int)threadIdx.x;
+    int e = -1;
+    if (f < hi) {
+      e = ids[f];
+      if (e < 0 || e >= E) e = -1;
+    }
+    const uint64_t peers = match_peers(e);
+    const int rank = __popcll(peers & below);
+    const bool leader = e >= 0 && rank == 0;
+    if (leader) cnt[w * E + e] = __popcll(peers);
+    __syncthreads();
+    if (e >= 0) {
+      int pos = next[e] + rank;
+      for (int w2 = 0; w2 < w; ++w2) pos += cnt[w2 * E + e];
+      sorted_ids[pos] = f;
+    }
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&next[e], __popcll(peers));
+      cnt[w * E + e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+// Exclusive scan of padded[0..E) into padded[] itself and offsets[], with
+// padded[E] = offsets[E] = total (wave 0 only; each lane owns a run).
+__device__ void scan_experts(int32_t* padded, int32_t* offsets, int E) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const int per = (E + 63) / 64;
+  const int lo = min(lane * per, E), hi = min(lo + per, E);
+  int sum = 0;
+  for (int e = lo; e < hi; ++e) sum += padded[e];
+  int incl = sum;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  int run = incl - sum;
+  for (int e = lo; e < hi; ++e) {
+    const int pe = padded[e];
+    offsets[e] = run;
+    padded[e] = run;
+    run += pe;
+  }
+  if (lane == 63) {
+    offsets[E] = run;
+    padded[E] = run;
+  }
+}
+
+// Sentinels in pad slots, the block -> expert map and the header.
+// start[0..E] holds the scanned offsets; counts the per-expert rows.
+__device__ void fill_padding(int32_t* routing, const int32_t* start, const int32_t* counts, int E,
+                             int B, int T, int topk, int cap, int nblocks, int nchunks,
+                             int32_t* sorted_ids, int32_t* block_expert) {
+  const int sentinel = T * topk;
+  const int total = start[E];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int s0 = start[e], s1 = start[e + 1];
+    for (int q = s0 + counts[e]; q < s1; ++q) sorted_ids[q] = sentinel;
+    for (int b = s0 / B; b < s1 / B; ++b) block_expert[b] = e;
+  }
+  for (int q = total + threadIdx.x; q < cap; q += blockDim.x) sorted_ids[q] = sentinel;
+  for (int b = total / B + threadIdx.x; b < nblocks; b += blockDim.x) block_expert[b] = -1;
+  if (threadIdx.x == 0) {
+    routing[HDR_MAGIC] = kRoutingMagic;
+    routing[HDR_BLOCK] = B;
+    routing[HDR_E] = E;
+    routing[HDR_T] = T;
+    routing[HDR_TOPK] = topk;
+    routing[HDR_CAP] = cap;
+    routing[HDR_NBLOCKS] = nblocks;
+    routing[HDR_TOTAL] = total;
+    routing[HDR_NCHUNKS] = nchunks;
+  }
+}
+
+// ---- small path: everything in one workgroup ------------------------------
+__global__ __launch_bounds__(1024) void align_small(const int32_t* __restrict__ ids, int E, int B,
+                                                    int T, int topk, int cap, int nblocks,
+                                                    int32_t* __restrict__ routing,
+                                                    int64_t off_counts, int64_t off_offsets,
+                                                    int64_t off_sorted, int64_t off_be) {
+  extern __shared__ int32_t smem[];
+  int32_t* hist = smem;                  // [E + 1]: counts, then next free slot
+  int32_t* start = smem + (E + 1);       // [E + 1]: padded counts, then offsets
+  int32_t* cnt = smem + 2 * (E + 1);     // [16][E]
+  int32_t* counts = routing + off_counts;
+  const int n = T * topk;
+  for (int i = threadIdx.x; i < 2 * (E + 1) + 16 * E; i += 1024) smem[i] = 0;
+  __syncthreads();
+  for (int f = threadIdx.x; f < n; f += 1024) {
+    const int e = ids[f];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    counts[e] = hist[e];
+    start[e] = (hist[e] + B - 1) / B * B;
+  }
+  __syncthreads();
+  scan_experts(start, routing + off_offsets, E);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 1024) hist[e] = start[e];
+  fill_padding(routing, start, counts, E, B, T, topk, cap, nblocks, 0, routing + off_sorted,
+               routing + off_be);
+  __syncthreads();
+  place_rows<16>(ids, 0, n, E, hist, cnt, routing + off_sorted);
+}
+
+// ---- large path ------------------------------------------------------------
 __global__ __launch_bounds__(kCountThreads) void align_count(const int32_t* __restrict__ ids,
                                                              int n, int E,
                                                              int32_t* __restrict__ chunk_hist) {
@@ -52,12 +196,7 @@ __global__ __launch_bounds__(kScanThreads) void align_scan(int32_t* __restrict__
                                                            int64_t off_scratch) {
   extern __shared__ int32_t padded[];   // [E + 1]
   int32_t* counts = routing + off_counts;
-  int32_t* offsets = routing + off_offsets;
-  int32_t* sorted_ids = routing + off_sorted;
-  int32_t* block_expert = routing + off_be;
   int32_t* chunk_hist = routing + off_scratch;
-  const int sentinel = T * topk;
-
   // per expert: exclusive prefix over chunks (in place) and the total
   for (int e = threadIdx.x; e < E; e += kScanThreads) {
     int run = 0;
@@ -70,94 +209,28 @@ __global__ __launch_bounds__(kScanThreads) void align_scan(int32_t* __restrict__
     padded[e] = (run + B - 1) / B * B;
   }
   __syncthreads();
-
-  // exclusive scan of padded counts over experts: wave 0, each lane owns a
-  // contiguous run of experts
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int per = (E + 63) / 64;
-    const int lo = min(lane * per, E), hi = min(lo + per, E);
-    int sum = 0;
-    for (int e = lo; e < hi; ++e) sum += padded[e];
-    int incl = sum;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    int run = incl - sum;
-    for (int e = lo; e < hi; ++e) {
-      const int p = padded[e];
-      offsets[e] = run;
-      padded[e] = run;       // reuse as the start offset
-      run += p;
-    }
-    if (lane == 63) {
-      offsets[E] = run;
-      padded[E] = run;
-      routing[HDR_TOTAL] = run;
-    }
-  }
+  scan_experts(padded, routing + off_offsets, E);
   __syncthreads();
-  const int total = padded[E];
-
-  // sentinel in every pad slot, block -> expert map
-  for (int e = threadIdx.x; e < E; e += kScanThreads) {
-    const int start = padded[e], end = padded[e + 1];
-    for (int p = start + counts[e]; p < end; ++p) sorted_ids[p] = sentinel;
-    for (int b = start / B; b < end / B; ++b) block_expert[b] = e;
-  }
-  for (int p = total + threadIdx.x; p < cap; p += kScanThreads) sorted_ids[p] = sentinel;
-  for (int b = total / B + threadIdx.x; b < nblocks; b += kScanThreads) block_expert[b] = -1;
-  if (threadIdx.x == 0) {
-    routing[HDR_MAGIC] = kRoutingMagic;
-    routing[HDR_BLOCK] = B;
-    routing[HDR_E] = E;
-    routing[HDR_T] = T;
-    routing[HDR_TOPK] = topk;
-    routing[HDR_CAP] = cap;
-    routing[HDR_NBLOCKS] = nblocks;
-    routing[HDR_NCHUNKS] = nchunks;
-  }
+  fill_padding(routing, padded, counts, E, B, T, topk, cap, nblocks, nchunks, routing + off_sorted,
+               routing + off_be);
 }
 
-__global__ __launch_bounds__(64) void align_scatter(const int32_t* __restrict__ ids, int n, int E,
-                                                    int32_t* __restrict__ routing,
-                                                    int64_t off_offsets, int64_t off_sorted,
-                                                    int64_t off_scratch) {
-  extern __shared__ int32_t next[];   // [E]: next free slot of each expert in this chunk
-  const int lane = threadIdx.x;
+template <int NWAVES>
+__global__ __launch_bounds__(NWAVES * 64) void align_scatter(const int32_t* __restrict__ ids, int n,
+                                                            int E, int32_t* __restrict__ routing,
+                                                            int64_t off_offsets, int64_t off_sorted,
+                                                            int64_t off_scratch) {
+  extern __shared__ int32_t smem[];
+  int32_t* next = smem;          // [E]
+  int32_t* cnt = smem + E;       // [NWAVES][E]
   const int chunk = blockIdx.x;
   const int32_t* offsets = routing + off_offsets;
   const int32_t* prefix = routing + off_scratch + (size_t)chunk * E;
-  int32_t* sorted_ids = routing + off_sorted;
-  for (int e = lane; e < E; e += 64) next[e] = offsets[e] + prefix[e];
+  for (int e = threadIdx.x; e < E; e += NWAVES * 64) next[e] = offsets[e] + prefix[e];
+  for (int i = threadIdx.x; i < NWAVES * E; i += NWAVES * 64) cnt[i] = 0;
   __syncthreads();
-  const int base = chunk * kAlignChunk;
-  for (int sb = 0; sb < kAlignChunk; sb += 64) {
-    const int f = base + sb + lane;
-    int e = -1;
-    if (f < n) {
-      e = ids[f];
-      if (e < 0 || e >= E) e = -1;
-    }
-    // lanes of this 64-row step routed to the same expert
-    uint64_t peers = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int ej = __shfl(e, j, 64);
-      peers |= (uint64_t)(ej == e) << j;
-    }
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int rank = __popcll(peers & below);
-    const int cnt = __popcll(peers);
-    int slot = 0;
-    if (e >= 0) slot = next[e] + rank;
-    __syncthreads();
-    if (e >= 0) {
-      sorted_ids[slot] = f;
-      if (rank == cnt - 1) next[e] = slot + 1;   // one writer per expert
-    }
-    __syncthreads();
-  }
+  const int lo = chunk * kAlignChunk;
+  place_rows<NWAVES>(ids, lo, min(n, lo + kAlignChunk), E, next, cnt, routing + off_sorted);
 }
 
 __global__ __launch_bounds__(256) void permute_rows(const uint16_t* __restrict__ x, int topk, int H,
@@ -191,6 +264,13 @@ __global__ __launch_bounds__(256) void permute_rows(const uint16_t* __restrict__
 hipError_t launch_align(const int32_t* topk_ids, int T, int topk, int E, const RoutingLayout& L,
                         int32_t* routing, hipStream_t s) {
   const int n = T * topk;
+  if (n <= kSmallMaxRows && E <= kSmallMaxExperts) {
+    const size_t lds = (size_t)(2 * (E + 1) + 16 * E) * sizeof(int32_t);
+    hipLaunchKernelGGL(align_small, dim3(1), dim3(1024), lds, s, topk_ids, E, L.block, T, topk, L.cap,
+                       L.nblocks, routing, L.off_counts, L.off_offsets, L.off_sorted,
+                       L.off_block_expert);
+    return hipGetLastError();
+  }
   const size_t lds_e = (size_t)E * sizeof(int32_t);
   if (L.nchunks > 0) {
     hipLaunchKernelGGL(align_count, dim3(L.nchunks), dim3(kCountThreads), lds_e, s, topk_ids, n, E,
@@ -200,8 +280,12 @@ hipError_t launch_align(const int32_t* topk_ids, int T, int topk, int E, const R
                      E, L.block, T, topk, L.nchunks, L.cap, L.nblocks, L.off_counts, L.off_offsets,
                      L.off_sorted, L.off_block_expert, L.off_scratch);
   if (L.nchunks > 0) {
-    hipLaunchKernelGGL(align_scatter, dim3(L.nchunks), dim3(64), lds_e, s, topk_ids, n, E, routing,
-                       L.off_offsets, L.off_sorted, L.off_scratch);
+    if (E <= 2048)   // 4 waves per chunk: 5 E ints of LDS
+      hipLaunchKernelGGL(align_scatter<4>, dim3(L.nchunks), dim3(256), 5 * lds_e, s, topk_ids, n, E,
+                         routing, L.off_offsets, L.off_sorted, L.off_scratch);
+    else
+      hipLaunchKernelGGL(align_scatter<1>, dim3(L.nchunks), dim3(64), 2 * lds_e, s, topk_ids, n, E,
+                         routing, L.off_offsets, L.off_sorted, L.off_scratch);
   }
   return hipGetLastError();
 }

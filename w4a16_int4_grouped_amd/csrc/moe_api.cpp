@@ -415,7 +415,7 @@ moe_status_t moe_prepare_weights(const moe_weight_desc_t* desc, const int32_t* w
   if (e != hipSuccess) return hip_fail(e, "prepare synchronise");
   if (bad)
     return fail(MOE_ERR_UNSUPPORTED_SCHEMA,
-                "a scale is NaN, infinite or of magnitude >= 2^124 (outside the supported range)");
+                "a scale is NaN, infinite or of magnitude >= 2^117 (outside the supported range)");
   moe_weights* h = new moe_weights();
   h->desc = *desc;
   h->lay = L;
@@ -585,8 +585,6 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   const int H = h->desc.hidden, I = h->desc.inter, E = h->desc.num_experts;
   uint16_t* a_ws = (uint16_t*)(wsb + W.off_a);
   float* acc = (float*)(wsb + W.off_acc);
-  if (e == hipSuccess) e = run("zero_acc", s, [&] { return launch_zero_f32(acc, (size_t)T * H, s); });
-
   GemmParams p{};
   p.counts = rt + R.off_counts;
   p.offsets = rt + R.off_offsets;
@@ -605,6 +603,8 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   p13.gather = 1;
   p13.a_out = a_ws;
   p13.a_ld = I;
+  p13.zero_ptr = acc;                    // T*H is a multiple of 4 (H % 32 == 0)
+  p13.zero_n4 = (int64_t)T * H / 4;
   if (e == hipSuccess)
     e = run("gemm_w13_small_m", s, [&] { return launch_gemm_small_m(p13, SET_INDEXED, EPI_SWIGLU, sc.nt, s); });
 
@@ -656,7 +656,6 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
   uint16_t* a_ws = (uint16_t*)(wsb + W.off_a);
   float* acc = (float*)(wsb + W.off_acc);
   hipError_t e = hipSuccess;
-  if (row_src && T > 0) e = run("zero_acc", s, [&] { return launch_zero_f32(acc, (size_t)T * H, s); });
 
   GemmParams p{};
   p.m_indices = m_indices;
@@ -673,6 +672,10 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
   p13.src_ld = H;
   p13.a_out = a_ws;
   p13.a_ld = I;
+  if (row_src && T > 0) {
+    p13.zero_ptr = acc;
+    p13.zero_n4 = (int64_t)T * H / 4;
+  }
   if (e == hipSuccess)
     e = run("gemm_w13_small_m", s, [&] { return launch_gemm_small_m(p13, SET_BLOCKS, EPI_SWIGLU, sc.nt, s); });
 

@@ -26,41 +26,79 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// v_cvt_off_f32_i4 on byte n of v (SDWA operand select): bits [3:0] of that
-// byte, read as a signed 4-bit integer i, become the float i / 16 (exact).
-#define MOE_CVT_OFF_BYTE(SEL)                                                         \
-  __device__ __forceinline__ float cvt_off_##SEL(uint32_t v) {                        \
-    float r;                                                                          \
-    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:" #SEL \
-        : "=v"(r)                                                                     \
-        : "v"(v));                                                                    \
-    return r;                                                                         \
-  }
-MOE_CVT_OFF_BYTE(BYTE_0)
-MOE_CVT_OFF_BYTE(BYTE_1)
-MOE_CVT_OFF_BYTE(BYTE_2)
-MOE_CVT_OFF_BYTE(BYTE_3)
-#undef MOE_CVT_OFF_BYTE
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
-// Dequantise one prepared word: eight uint4 values q, low nibble first along
-// K, stored as q ^ 8 (which, read as a signed 4-bit integer, is q - 8), with
-// the group scale given as s16 = 16 * s (Chord page, "H200 and Blackwell
-// indexed decode": subtract-then-scale fused into the nibble extraction,
-// keeping the unfused BF16 rounding order).
+// (v & mask) | magic in one VOP3 instruction (the compiler would emit an AND
+// and an OR). The mask lives in an SGPR, the magic constant in a VGPR (one
+// scalar operand per VOP3 instruction on gfx9).
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask), "v"(magic));
+  return r;
+}
+
+// Per-group constants of dq8: the scale s, s/16, -1032 s and -72 s (all
+// exact for |s| < 2^117, subnormal s included).
+struct GroupScale {
+  float s, s16, c0, c1;
+};
+
+__device__ __forceinline__ GroupScale group_scale(float s) {
+  return GroupScale{s, s * 0.0625f, s * -1032.0f, s * -72.0f};
+}
+
+// Dequantise one packed word: eight uint4 values q, low nibble first along
+// K, with the group scale s (Chord page, "H200 and Blackwell indexed
+// decode": subtract-then-scale fused into the nibble extraction, keeping the
+// unfused BF16 rounding order).
 //
-// v_cvt_off_f32_i4 gives (q - 8) / 16 exactly, the product with 16 * s is
-// exactly (q - 8) * s (at most 4 + 8 significant bits, signed zeros
-// included), and v_cvt_pk_bf16_f32 rounds it once to BF16: bit-identical to
-// bf16_rne((q - 8) * s). The low nibble of each byte is read in place; the
-// high nibbles after one 4-bit shift of the word.
-// Result dword m holds k = 2m (low half) and k = 2m+1 (high half).
-__device__ __forceinline__ u32x4_t dq8(uint32_t w, float s16) {
-  const uint32_t h = w >> 4;
+// Nibbles 0 and 4 masked into the mantissas of an FP16 pair with exponent
+// bits 0x6400 read as 1024 + q; nibbles 1 and 5, masked in place one nibble
+// higher, read as 1024 + 16 q; nibbles 2, 6 and 3, 7 likewise after one
+// 8-bit shift. v_fma_mix_f32 widens one FP16 half and computes
+//   (1024 + q) s - 1032 s   or   (1024 + 16 q) (s/16) - 72 s,
+// exactly (q - 8) s before its single rounding, and (q - 8) s has at most
+// 4 + 8 significant bits, so the FP32 result is exact; v_cvt_pk_bf16_f32
+// then rounds it once to BF16: bf16_rne((q - 8) s) for every nonzero
+// product. An exactly zero product comes out as +0 whatever the signs
+// (x - x = +0); no MFMA result can tell +0 from -0 here, since the
+// accumulators start at +0 and +0 + -0 = +0. 17 VALU instructions per 8
+// weights. Result dword m holds k = 2m (low half) and k = 2m+1 (high half).
+__device__ __forceinline__ u32x4_t dq8(uint32_t w, const GroupScale& g, uint32_t magic) {
+  const uint32_t w8 = w >> 8;
+  const f16x2_t r0 = __builtin_bit_cast(f16x2_t, and_or(w, 0x000F000Fu, magic));    // q0, q4
+  const f16x2_t r1 = __builtin_bit_cast(f16x2_t, and_or(w, 0x00F000F0u, magic));    // q1, q5
+  const f16x2_t r2 = __builtin_bit_cast(f16x2_t, and_or(w8, 0x000F000Fu, magic));   // q2, q6
+  const f16x2_t r3 = __builtin_bit_cast(f16x2_t, and_or(w8, 0x00F000F0u, magic));   // q3, q7
   u32x4_t r;
-  r[0] = pack_bf16x2(cvt_off_BYTE_0(w) * s16, cvt_off_BYTE_0(h) * s16);
-  r[1] = pack_bf16x2(cvt_off_BYTE_1(w) * s16, cvt_off_BYTE_1(h) * s16);
-  r[2] = pack_bf16x2(cvt_off_BYTE_2(w) * s16, cvt_off_BYTE_2(h) * s16);
-  r[3] = pack_bf16x2(cvt_off_BYTE_3(w) * s16, cvt_off_BYTE_3(h) * s16);
+  r[0] = pack_bf16x2(__builtin_fmaf((float)r0[0], g.s, g.c0), __builtin_fmaf((float)r1[0], g.s16, g.c1));
+  r[1] = pack_bf16x2(__builtin_fmaf((float)r2[0], g.s, g.c0), __builtin_fmaf((float)r3[0], g.s16, g.c1));
+  r[2] = pack_bf16x2(__builtin_fmaf((float)r0[1], g.s, g.c0), __builtin_fmaf((float)r1[1], g.s16, g.c1));
+  r[3] = pack_bf16x2(__builtin_fmaf((float)r2[1], g.s, g.c0), __builtin_fmaf((float)r3[1], g.s16, g.c1));
+  return r;
+}
+
+constexpr uint32_t kF16Magic = 0x64006400u;   // two FP16 1024.0
+
+// dq8 with the sign of zero products set as in (q - 8) * s (sign of q - 8
+// times sign of s, +0 for q = 8 with s > 0): bit-identical to
+// bf16_rne((q - 8) * s) everywhere. Used where the dequantised weights
+// themselves are the result.
+__device__ __forceinline__ u32x4_t dq8_exact(uint32_t w, const GroupScale& g) {
+  u32x4_t r = dq8(w, g, kF16Magic);
+  const uint32_t s_neg = (__float_as_uint(g.s) >> 31) & 1u;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t q = (w >> (4 * (2 * m + h))) & 0xFu;
+      const uint32_t bits = (r[m] >> (16 * h)) & 0xFFFFu;
+      if ((bits & 0x7FFFu) == 0u) {
+        const uint32_t neg = (q < 8u ? 1u : 0u) ^ s_neg;
+        r[m] = (r[m] & ~(0xFFFFu << (16 * h))) | ((neg << 15) << (16 * h));
+      }
+    }
+  }
   return r;
 }
 

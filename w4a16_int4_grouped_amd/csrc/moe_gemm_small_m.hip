@@ -8,18 +8,25 @@
 //
 // Work item: one row set (an expert, or a 128-row block of the contiguous
 // layout) x 256 weight rows. Each of the 4 waves owns one row group of 64
-// weight rows (4 MFMA tiles) over the whole K, and loops over the set's rows
-// 16*NT at a time, so an expert's weights are streamed once whenever its
-// rows fit in 16*NT. The grid is fixed from host-known sizes and each
-// workgroup reads its row count on the device (a semi-static token-tile
+// weight rows (4 MFMA tiles) over the whole K, and the workgroup loops over
+// the set's rows 16*NT at a time, so an expert's weights are streamed once
+// whenever its rows fit in 16*NT. The grid is fixed from host-known sizes and
+// each workgroup reads its row count on the device (a semi-static token-tile
 // schedule, the variant the Chord page measured faster than a fully dynamic
 // one in "H200 and Blackwell indexed decode").
 //
-// Per K chunk of 128, lane l loads 16 contiguous bytes of each of its 4
-// tiles (one coalesced 1 KB wave load per tile), one dword pair of scales
-// and 64 contiguous bytes of each token row it feeds; all of lane l's 32 k
-// values of a tile share one scale group. Loads of chunk kc+1 are issued
-// before the dequantisation and MFMAs of chunk kc.
+// Per K chunk of 128:
+//   * each wave streams 4 KB of its packed weights (one coalesced 1 KB load
+//     per tile) and 512 B of scales, two chunks ahead of the math, in three
+//     rotating register buffers (about 9 KB in flight per wave, enough to
+//     keep HBM busy at four waves per SIMD);
+//   * the workgroup loads the token tile (16*NT rows x 128 k of BF16) once,
+//     one chunk ahead, through registers into one of three LDS buffers
+//     (rows padded to 272 B so the fragment reads hit 64 distinct banks);
+//   * every lane's 32 k values of a tile share one scale group, so each
+//     (lane, tile, chunk) needs one scale.
+// Loads past the last chunk go to a valid dummy address, so every load in
+// the loop is unconditional and each wait covers exactly the buffer in use.
 //
 // Epilogues: SwiGLU into the BF16 intermediate (W13, gate/up tiles
 // interleaved so both halves of a column sit in the same lane and register),
@@ -34,64 +41,100 @@ namespace moe {
 
 namespace {
 
-template <int NT>
-struct Frags {
+constexpr int kBRow = 136;   // LDS token row: 128 BF16 + 8 pad (272 B)
+
+struct AFrag {
   u32x4_t A[kMT];
   u32x2_t S;
-  u32x4_t B[NT][4];
 };
 
-template <int NT, bool TAIL>
-__device__ __forceinline__ void load_chunk(Frags<NT>& f, const u32x4_t* __restrict__ wq,
-                                           const u32x2_t* __restrict__ ws,
-                                           const uint16_t* const (&brow)[NT], int kc, int klim,
-                                           int kq) {
+template <int NT>
+struct TileLds {
+  uint16_t b[3][NT][16][kBRow];
+};
+
+// wq / ws: the wave's chunk base (wave-uniform, kept in SGPRs); lane: the
+// per-lane element offset.
+__device__ __forceinline__ void load_a(AFrag& f, const u32x4_t* __restrict__ wq,
+                                       const u32x2_t* __restrict__ ws, int lane) {
+  // weights and scales are streamed once: nontemporal loads keep them from
+  // displacing activation rows in L2
 #pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) f.A[mt] = wq[(kc * kMT + mt) * 64];
-  f.S = ws[kc * 64];
+  for (int mt = 0; mt < kMT; ++mt) f.A[mt] = __builtin_nontemporal_load(wq + mt * 64 + lane);
+  f.S = __builtin_nontemporal_load(ws + lane);
+}
+
+template <int NT>
+__device__ __forceinline__ void load_b(u32x4_t (&st)[NT], const uint16_t* const (&lrow)[NT], int kc,
+                                       int kmax) {
+  // this thread's 16-byte piece of each token row; k past K reads zero (the
+  // substitute address is the row's first element, always valid)
+  const int lpiece = (threadIdx.x & 15) * 8;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (!TAIL) {
-        f.B[nt][g] = *reinterpret_cast<const u32x4_t*>(brow[nt] + kc * kKC + g * 8);
-      } else {
-        // k past K: zero the activation (the prepared weights there are 0)
-        // (the substitute address is the row's first element, always valid)
-        const bool ok = g * 8 < klim;
-        const uint16_t* src = ok ? brow[nt] + kc * kKC + g * 8 : brow[nt] - kq;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src);
-        const u32x4_t z = {0u, 0u, 0u, 0u};
-        f.B[nt][g] = ok ? v : z;
-      }
-    }
+    const bool ok = kc * kKC < kmax;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lrow[nt] + (ok ? kc * kKC : -lpiece));
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    st[nt] = ok ? v : z;
   }
 }
 
 template <int NT>
-__device__ __forceinline__ void mma_chunk(const Frags<NT>& f, f32x4_t (&acc)[kMT][NT]) {
-  const float s16[4] = {bf16_lo(f.S[0]), bf16_hi(f.S[0]), bf16_lo(f.S[1]), bf16_hi(f.S[1])};
+__device__ __forceinline__ void store_b(TileLds<NT>& lds, int buf, const u32x4_t (&st)[NT]) {
+  const int r = threadIdx.x >> 4, piece = threadIdx.x & 15;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+    *reinterpret_cast<u32x4_t*>(&lds.b[buf][nt][r][piece * 8]) = st[nt];
+}
+
+template <int NT>
+__device__ __forceinline__ void mma_chunk(const AFrag& f, const TileLds<NT>& lds, int buf,
+                                          f32x4_t (&acc)[kMT][NT], uint32_t magic) {
+  const int lane = threadIdx.x & 63;
+  const uint16_t* brow = &lds.b[buf][0][lane & 15][(lane >> 4) * 32];
+  const float sc[4] = {bf16_lo(f.S[0]), bf16_hi(f.S[0]), bf16_lo(f.S[1]), bf16_hi(f.S[1])};
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) {
+    const GroupScale gs = group_scale(sc[mt]);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const u32x4_t a = dq8(f.A[mt][g], s16[mt]);
+      // token fragments are re-read from LDS per step to keep registers low
+      u32x4_t bf[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16(a, f.B[nt][g], acc[mt][nt]);
+      for (int nt = 0; nt < NT; ++nt)
+        bf[nt] = *reinterpret_cast<const u32x4_t*>(brow + nt * (16 * kBRow) + g * 8);
+      const u32x4_t a = dq8(f.A[mt][g], gs, magic);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16(a, bf[nt], acc[mt][nt]);
     }
   }
 }
 
+// Occupancy target per token-tile count: 4 workgroups (4 waves per SIMD) fit
+// NT = 1 in 128 registers without spilling; wider tiles need more registers.
+template <int NT>
+constexpr int kSmallMBlocksPerCU = NT == 1 ? 4 : (NT == 2 ? 3 : 2);
+
 template <int NT, int SET, int EPI>
-__global__ __launch_bounds__(256) void gemm_small_m(const GemmParams p) {
+__global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(const GemmParams p) {
   constexpr bool kGather = (SET == SET_INDEXED && EPI == EPI_SWIGLU);
+  __shared__ TileLds<NT> lds;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  if (p.zero_ptr) {   // clear the combine accumulator the next GEMM adds into
+    const int64_t per = (p.zero_n4 + p.total_wg - 1) / p.total_wg;
+    const int64_t lo = (int64_t)blockIdx.x * per;
+    const int64_t hi = min(lo + per, p.zero_n4);
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) reinterpret_cast<f32x4_t*>(p.zero_ptr)[i] = z;
+  }
   const int logical = xcd_remap(blockIdx.x, p.total_wg);
   const int set = logical / p.wg_per_set;
-  const int rg = (logical - set * p.wg_per_set) * 4 + wave;
-  if (rg >= p.RG) return;
+  const int rg_raw = (logical - set * p.wg_per_set) * 4 + wave;
+  const bool active = rg_raw < p.RG;          // waves past the last row group still load tiles
+  const int rg = active ? rg_raw : p.RG - 1;
 
+  // ---- the row set (uniform over the workgroup)
   int e, slot0, count;
   if constexpr (SET == SET_INDEXED) {
     const int32_t* hdr = p.routing_hdr;
@@ -114,25 +157,30 @@ __global__ __launch_bounds__(256) void gemm_small_m(const GemmParams p) {
       if (v >= 0 && v < p.E) m = max(m, v);
     }
     e = wave_max(m);
-    if (e < 0) return;   // all padding
   }
-  if (count <= 0) return;
+  if (count <= 0 || e < 0) return;
 
   const size_t tile0 = ((size_t)e * p.RG + rg) * p.Kc;
-  const u32x4_t* __restrict__ wq = reinterpret_cast<const u32x4_t*>(p.wq) + tile0 * (kMT * 64) + lane;
-  const u32x2_t* __restrict__ ws = reinterpret_cast<const u32x2_t*>(p.wsc) + tile0 * 64 + lane;
-  const int kq = (lane >> 4) * 32;            // this lane's k offset inside a chunk
-  const int kfull = p.K / kKC;                // chunks without a K tail
-  const int tail_lim = p.K - kfull * kKC - kq; // valid k of this lane in the tail chunk
+  const size_t cstride = 1;   // tiles between consecutive chunks of a row group
+  const u32x4_t* __restrict__ wq = reinterpret_cast<const u32x4_t*>(p.wq) + tile0 * (kMT * 64);
+  const u32x2_t* __restrict__ ws = reinterpret_cast<const u32x2_t*>(p.wsc) + tile0 * 64;
+  // dummy source for prefetches past the last chunk (valid, quickly cached)
+  const u32x4_t* __restrict__ wq_dummy = reinterpret_cast<const u32x4_t*>(p.wq);
+  const u32x2_t* __restrict__ ws_dummy = reinterpret_cast<const u32x2_t*>(p.wsc);
+  const int Kc = p.Kc;
+  const uint32_t magic = kF16Magic;
+  const int lr = threadIdx.x >> 4;             // token row this thread loads into LDS
+  const int lpiece = (threadIdx.x & 15) * 8;   // its k offset within a chunk
+  const int kmax = p.K - lpiece;               // chunk kc is readable if kc*128 < kmax
 
   for (int tb = 0; tb < count; tb += 16 * NT) {
-    const uint16_t* brow[NT];
+    const uint16_t* lrow[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int r = min(tb + nt * 16 + (lane & 15), count - 1);   // pad columns repeat a valid row
+      const int r = min(tb + nt * 16 + lr, count - 1);   // pad columns repeat a valid row
       const int slot = slot0 + r;
       const int row = kGather ? p.sorted_ids[slot] / p.topk : slot;
-      brow[nt] = p.src + (size_t)row * p.src_ld + kq;
+      lrow[nt] = p.src + (size_t)row * p.src_ld + lpiece;
     }
     f32x4_t acc[kMT][NT];
 #pragma unroll
@@ -140,15 +188,40 @@ __global__ __launch_bounds__(256) void gemm_small_m(const GemmParams p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    Frags<NT> cur, nxt;
-    if (kfull > 0) load_chunk<NT, false>(cur, wq, ws, brow, 0, 0, kq);
-    else load_chunk<NT, true>(cur, wq, ws, brow, 0, tail_lim, kq);
-    for (int kc = 0; kc < p.Kc; ++kc) {
-      if (kc + 1 < kfull) load_chunk<NT, false>(nxt, wq, ws, brow, kc + 1, 0, kq);
-      else if (kc + 1 < p.Kc) load_chunk<NT, true>(nxt, wq, ws, brow, kc + 1, tail_lim, kq);
-      mma_chunk<NT>(cur, acc);
-      cur = nxt;
+    // prologue: weights of chunks 0 and 1, token tile of chunk 0
+    AFrag fr0, fr1, fr2;
+    u32x4_t st[NT];
+    load_b<NT>(st, lrow, 0, kmax);
+    load_a(fr0, wq, ws, lane);
+    load_a(fr1, Kc > 1 ? wq + cstride * (kMT * 64) : wq_dummy, Kc > 1 ? ws + cstride * 64 : ws_dummy,
+           lane);
+    __syncthreads();   // the previous pass's readers are done with the LDS tiles
+    store_b<NT>(lds, 0, st);
+    __syncthreads();
+
+    // step J computes chunk c from register buffer J and LDS buffer J, and
+    // prefetches chunk c+2 into register buffer (J+2)%3 and the token tile of
+    // chunk c+1 into LDS buffer (J+1)%3.
+#define MOE_SMALL_M_STEP(J, CUR, NXT2)                                                           \
+  {                                                                                              \
+    const int c = kc + J;                                                                        \
+    load_b<NT>(st, lrow, min(c + 1, Kc - 1), kmax);                                              \
+    const bool more = c + 2 < Kc;                                                                \
+    load_a(NXT2, more ? wq + (size_t)(c + 2) * cstride * (kMT * 64) : wq_dummy,                  \
+           more ? ws + (size_t)(c + 2) * cstride * 64 : ws_dummy, lane);                         \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    if (c < Kc) mma_chunk<NT>(CUR, lds, J, acc, magic);                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    store_b<NT>(lds, (J + 1) % 3, st);                                                           \
+    __syncthreads();                                                                             \
+  }
+    for (int kc = 0; kc < Kc; kc += 3) {
+      MOE_SMALL_M_STEP(0, fr0, fr2)
+      MOE_SMALL_M_STEP(1, fr1, fr0)
+      MOE_SMALL_M_STEP(2, fr2, fr1)
     }
+#undef MOE_SMALL_M_STEP
+    if (!active) continue;
 
     // ---- epilogue
 #pragma unroll

@@ -53,6 +53,10 @@ struct GemmParams {
   int64_t acc_ld;             // COMBINE
   uint16_t* out;
   int64_t out_ld;             // STORE
+  // optional: float4 words cleared by the kernel's workgroups before their
+  // tiles (the accumulator of a following COMBINE GEMM)
+  float* zero_ptr;
+  int64_t zero_n4;
 };
 
 hipError_t launch_gemm_small_m(const GemmParams& p, int set, int epi, int nt, hipStream_t s);

@@ -27,10 +27,8 @@ inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // k = 128*kc + 32*(l/16) + [0, 32): word g is the MFMA A fragment of step g
 // of the chunk, and all 32 values share one scale group.
 // Scales: u16[E][RG][Kc][64][kMT]: lane l's scale for tile mt.
-// Stored values: each nibble holds q ^ 8 (q - 8 as a signed 4-bit integer)
-// and each scale holds 16 * s as BF16 (exact), the operands of dq8.
-// Rows past N and k past K are padding: words 0 (q = 8, weight 0) and
-// scale 0.
+// Words and scales keep their canonical values. Rows past N and k past K are
+// padding: words 0x88888888 (q = 8, weight 0) and scale 0.
 struct MatLayout {
   int E = 0, N = 0, K = 0;   // true shape
   int RG = 0, Kc = 0;        // row groups, k chunks

@@ -7,7 +7,7 @@
 // kernels": the forward path reads pre-permuted INT4 bytes and re-tiled
 // scales). Each lane's 16 bytes of a prepared tile are four consecutive
 // canonical words of one row, so the repack is a 16-byte gather; no nibble
-// moves inside a word.
+// moves inside a word and words and scales keep their canonical values.
 #include <hip/hip_runtime.h>
 
 #include "moe_device.h"
@@ -33,12 +33,9 @@ __global__ __launch_bounds__(256) void repack_words(const uint32_t* __restrict__
   const size_t e = t / RG;
   const int row = canon_row(rg * kMT + mt, lane & 15, interleave_I);
   const int kword = kc * 16 + (lane >> 4) * 4;
-  // stored nibble = q ^ 8 (q - 8 as a signed 4-bit value); padding is q = 8
-  u32x4_t v = {0u, 0u, 0u, 0u};
-  if (row < N && kword * 8 < K) {
+  u32x4_t v = {0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};   // padding: q = 8
+  if (row < N && kword * 8 < K)
     v = *reinterpret_cast<const u32x4_t*>(canon + (e * N + row) * (size_t)(K / 8) + kword);
-    v ^= 0x88888888u;
-  }
   prep[idx] = v;
 }
 
@@ -57,15 +54,13 @@ __global__ __launch_bounds__(256) void repack_scales(const uint16_t* __restrict_
   const size_t e = t / RG;
   const int row = canon_row(rg * kMT + mt, lane & 15, interleave_I);
   const int grp = kc * 4 + (lane >> 4);
-  // stored scale = 16 * s (exact: a power-of-two scaling that stays finite)
-  uint16_t s16 = 0;
+  uint16_t s = 0;
   if (row < N && grp < K / 32) {
-    const uint16_t s = canon[(e * N + row) * (size_t)(K / 32) + grp];
-    // NaN, infinity or |s| >= 2^124 (where 16 s would overflow) are rejected
-    if ((s & 0x7FFF) >= 0x7D80) atomicOr(bad, 1);
-    s16 = (uint16_t)(__float_as_uint(__uint_as_float((uint32_t)s << 16) * 16.0f) >> 16);
+    s = canon[(e * N + row) * (size_t)(K / 32) + grp];
+    // NaN, infinity or |s| >= 2^117 (where -1032 s would overflow) are rejected
+    if ((s & 0x7FFF) >= 0x7A00) atomicOr(bad, 1);
   }
-  prep[idx] = s16;
+  prep[idx] = s;
 }
 
 // One thread per prepared lane-fragment (4 words = 32 weights of one row).
@@ -83,14 +78,14 @@ __global__ __launch_bounds__(256) void dequant_expert(const u32x4_t* __restrict_
   const int rg = t / Kc;
   const size_t tile = ((size_t)e * RG + rg) * Kc + kc;
   const u32x4_t A = wq[(tile * kMT + mt) * 64 + lane];
-  const float s16 = __uint_as_float((uint32_t)wsc[(tile * 64 + lane) * kMT + mt] << 16);
+  const GroupScale gs = group_scale(__uint_as_float((uint32_t)wsc[(tile * 64 + lane) * kMT + mt] << 16));
   const int row = canon_row(rg * kMT + mt, lane & 15, interleave_I);
   if (row >= N) return;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int k0 = kc * kKC + (lane >> 4) * 32 + g * 8;
     if (k0 < K)
-      *reinterpret_cast<u32x4_t*>(out + (size_t)row * K + k0) = dq8(A[g], s16);
+      *reinterpret_cast<u32x4_t*>(out + (size_t)row * K + k0) = dq8_exact(A[g], gs);
   }
 }
 
