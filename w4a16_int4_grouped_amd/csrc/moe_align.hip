@@ -109,7 +109,8 @@ __device__ void scan_experts(int32_t* padded, int32_t* offsets, int E) {
 }
 
 // Sentinels in pad slots, the block -> expert map and the header.
-// start[0..E] holds the scanned offsets; counts the per-expert rows.
+// start[0..E] holds the scanned offsets; counts the per-expert rows (NULL:
+// the caller has written the pad slots of each expert already).
 __device__ void fill_padding(int32_t* routing, const int32_t* start, const int32_t* counts, int E,
                              int B, int T, int topk, int cap, int nblocks, int nchunks,
                              int32_t* sorted_ids, int32_t* block_expert) {
@@ -117,7 +118,8 @@ __device__ void fill_padding(int32_t* routing, const int32_t* start, const int32
   const int total = start[E];
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const int s0 = start[e], s1 = start[e + 1];
-    for (int q = s0 + counts[e]; q < s1; ++q) sorted_ids[q] = sentinel;
+    if (counts)
+      for (int q = s0 + counts[e]; q < s1; ++q) sorted_ids[q] = sentinel;
     for (int b = s0 / B; b < s1 / B; ++b) block_expert[b] = e;
   }
   for (int q = total + threadIdx.x; q < cap; q += blockDim.x) sorted_ids[q] = sentinel;
@@ -136,6 +138,10 @@ __device__ void fill_padding(int32_t* routing, const int32_t* start, const int32
 }
 
 // ---- small path: everything in one workgroup ------------------------------
+// Thread t owns flat rows t, t + 1024, ... (at most kSmallRounds of them),
+// loaded once into registers for both the count and the placement.
+constexpr int kSmallRounds = kSmallMaxRows / 1024;
+
 __global__ __launch_bounds__(1024) void align_small(const int32_t* __restrict__ ids, int E, int B,
                                                     int T, int topk, int cap, int nblocks,
                                                     int32_t* __restrict__ routing,
@@ -146,26 +152,64 @@ __global__ __launch_bounds__(1024) void align_small(const int32_t* __restrict__ 
   int32_t* start = smem + (E + 1);       // [E + 1]: padded counts, then offsets
   int32_t* cnt = smem + 2 * (E + 1);     // [16][E]
   int32_t* counts = routing + off_counts;
+  int32_t* sorted_ids = routing + off_sorted;
   const int n = T * topk;
+  const int rounds = (n + 1023) / 1024;
+  int my_e[kSmallRounds];
+#pragma unroll
+  for (int r = 0; r < kSmallRounds; ++r) {
+    const int f = r * 1024 + (int)threadIdx.x;
+    int e = -1;
+    if (r < rounds && f < n) {
+      e = ids[f];
+      if (e < 0 || e >= E) e = -1;
+    }
+    my_e[r] = e;
+  }
   for (int i = threadIdx.x; i < 2 * (E + 1) + 16 * E; i += 1024) smem[i] = 0;
   __syncthreads();
-  for (int f = threadIdx.x; f < n; f += 1024) {
-    const int e = ids[f];
-    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
-  }
+#pragma unroll
+  for (int r = 0; r < kSmallRounds; ++r)
+    if (my_e[r] >= 0) atomicAdd(&hist[my_e[r]], 1);
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 1024) {
-    counts[e] = hist[e];
-    start[e] = (hist[e] + B - 1) / B * B;
-  }
+  for (int e = threadIdx.x; e < E; e += 1024) start[e] = (hist[e] + B - 1) / B * B;
   __syncthreads();
   scan_experts(start, routing + off_offsets, E);
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 1024) hist[e] = start[e];
-  fill_padding(routing, start, counts, E, B, T, topk, cap, nblocks, 0, routing + off_sorted,
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    counts[e] = hist[e];
+    const int s0 = start[e], s1 = start[e + 1];
+    for (int q = s0 + hist[e]; q < s1; ++q) sorted_ids[q] = T * topk;
+    hist[e] = s0;   // next free slot
+  }
+  fill_padding(routing, start, nullptr, E, B, T, topk, cap, nblocks, 0, sorted_ids,
                routing + off_be);
   __syncthreads();
-  place_rows<16>(ids, 0, n, E, hist, cnt, routing + off_sorted);
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+#pragma unroll
+  for (int r = 0; r < kSmallRounds; ++r) {
+    if (r >= rounds) break;   // uniform
+    const int e = my_e[r];
+    const uint64_t peers = match_peers(e);
+    const int rank = __popcll(peers & below);
+    const bool leader = e >= 0 && rank == 0;
+    if (leader) cnt[w * E + e] = __popcll(peers);
+    __syncthreads();
+    if (e >= 0) {
+      int pos = hist[e] + rank;
+      for (int w2 = 0; w2 < w; ++w2) pos += cnt[w2 * E + e];
+      sorted_ids[pos] = r * 1024 + (int)threadIdx.x;
+    }
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&hist[e], __popcll(peers));
+      cnt[w * E + e] = 0;
+    }
+    __syncthreads();
+  }
 }
 
 // ---- large path ------------------------------------------------------------
