@@ -34,7 +34,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=1, help="index into synth.WORKLOADS (indexed layouts)")
+    ap.add_argument("--workload", type=int, default=1,
+                    help="index into synth.WORKLOADS (1: the Kimi decode layer, the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=8, help="experts in the oracle's timed sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -113,26 +114,61 @@ def main():
     import w4a16_int4_grouped_amd as M
 
     wl = synth.WORKLOADS[args.workload]
-    if wl.layout != "indexed":
-        sys.exit("bench.py times the indexed layout workloads")
     log(f"workload {wl.name}: generating inputs")
     t = time.time()
     w = synth.stacked_weights(wl)
-    x = synth.activations(wl.iseed, wl.T, wl.H)
-    ids, tw = synth.routing(wl)
-    log(f"  generated in {time.time() - t:.1f} s; uploading and preparing")
+    log(f"  generated weights in {time.time() - t:.1f} s; uploading and preparing")
     dw = [to_dev(a, torch, np) for a in w]
-    h = M.PreparedWeights(*dw, mode="indexed")
+    h = M.PreparedWeights(*dw, mode=wl.layout)
     del dw
     torch.cuda.empty_cache()
-    x_d, ids_d, tw_d = to_dev(x, torch, np), to_dev(ids, torch, np), to_dev(tw, torch, np)
-    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(h.workspace_bytes(wl.T, wl.topk, wl.T), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    log(f"  schedule: {h.describe(wl.T, wl.topk)}")
+    x = ids = tw = None
 
-    def step():
-        h.indexed(x_d, ids_d, tw_d, out=out, ws=ws, stream=stream)
+    if wl.layout == "indexed":
+        x = synth.activations(wl.iseed, wl.T, wl.H)
+        ids, tw = synth.routing(wl)
+        x_d, ids_d, tw_d = to_dev(x, torch, np), to_dev(ids, torch, np), to_dev(tw, torch, np)
+        out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(h.workspace_bytes(wl.T, wl.topk, wl.T), dtype=torch.uint8, device="cuda")
+        log(f"  schedule: {h.describe(wl.T, wl.topk)}")
+        rows = wl.T * wl.topk
+        touched = int(np.unique(ids[(ids >= 0) & (ids < wl.E)]).size)
+
+        def step():
+            h.indexed(x_d, ids_d, tw_d, out=out, ws=ws, stream=stream)
+    elif wl.layout == "contiguous":
+        # the contiguous input comes from the library's own align (block 128) + permute
+        x = synth.activations(wl.iseed, wl.T, wl.H)
+        ids, tw = synth.routing(wl)
+        x_d, ids_d, tw_d = to_dev(x, torch, np), to_dev(ids, torch, np), to_dev(tw, torch, np)
+        hi = M.PreparedWeights(*[to_dev(a, torch, np) for a in synth.stacked_weights(
+            synth.scaled(wl, I=32))], mode="indexed")   # align + permute only need E and H
+        ovr = {"block_m": 128}
+        routing = hi.align(ids_d, ovr=ovr)
+        a_d, m_d, src_d = hi.permute(x_d, wl.topk, routing, ovr=ovr)
+        total = int(routing[7].item())
+        a_d, m_d, src_d = a_d[:total].contiguous(), m_d[:total].contiguous(), src_d[:total].contiguous()
+        del hi, routing
+        out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(h.workspace_bytes(total, wl.topk, wl.T), dtype=torch.uint8, device="cuda")
+        log(f"  M_pad={total}; schedule: {h.describe(total)}")
+        rows = wl.T * wl.topk
+        touched = int(np.unique(ids).size)
+
+        def step():
+            h.contiguous(a_d, m_d, src_d, tw_d, wl.T, wl.topk, out=out, ws=ws, stream=stream)
+    else:
+        a3, mm = synth.masked_inputs(wl)
+        a3_d, mm_d = to_dev(a3, torch, np), to_dev(mm, torch, np)
+        out = torch.empty((wl.E * wl.max_m, wl.H), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(h.workspace_bytes(wl.max_m), dtype=torch.uint8, device="cuda")
+        log(f"  schedule: {h.describe(wl.max_m, expected_m=wl.expected_m)}")
+        rows = int(mm.sum())
+        touched = int((mm > 0).sum())
+
+        def step():
+            h.masked(a3_d, mm_d, wl.expected_m, out=out, ws=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -151,15 +187,26 @@ def main():
     kernels = M.profile_read()
     log("  kernels (avg us): " + ", ".join(f"{k}={v[1] / v[0] * 1e3:.1f}" for k, v in sorted(kernels.items())))
 
-    # roofline of the dominant kernel: W13 grouped GEMM, bound by HBM on its
-    # packed weight bytes (every touched expert's W13 is streamed once)
-    touched = int(np.unique(ids[(ids >= 0) & (ids < wl.E)]).size)
-    dom = "gemm_w13_small_m"
+    # dominant kernel: the W13 grouped GEMM. Few rows per expert: bound by HBM
+    # on its packed weight bytes (every touched expert's W13 streamed once).
+    # Many rows per expert: bound by MFMA on valid-row flops (4*H*I per row).
+    dom = next((k for k in kernels if k.startswith("gemm_w13")), "gemm_w13")
     n, tot_ms = kernels.get(dom, (0, 0.0))
     dom_us = tot_ms / max(n, 1) * 1e3
-    w13_bytes = touched * wl.H * wl.I           # 2I rows x H/2 bytes
-    achieved = w13_bytes / (dom_us * 1e-6) / 1e9 if dom_us > 0 else 0.0
+    rows_per_expert = rows / max(touched, 1)
     layer_packed = touched * 1.5 * wl.H * wl.I
+    layer_flops = rows * 6.0 * wl.H * wl.I
+    if rows_per_expert < 80:
+        work = touched * wl.H * wl.I            # packed W13 bytes: 2I rows x H/2 bytes
+        achieved = work / (dom_us * 1e-6) / 1e9 if dom_us > 0 else 0.0
+        roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "avg_us": dom_us, "bytes_per_launch": work}
+    else:
+        work = rows * 4.0 * wl.H * wl.I         # valid-row W13 flops
+        achieved = work / (dom_us * 1e-6) / 1e12 if dom_us > 0 else 0.0
+        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "avg_us": dom_us,
+                "flops_per_launch": work}
     result = {
         "metric": METRIC,
         "value": ms * 1e3,
@@ -174,15 +221,16 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "layout": wl.layout, "experts": wl.E, "hidden": wl.H,
-                   "intermediate": wl.I, "tokens": wl.T, "topk": wl.topk,
-                   "weights": "uint4 g32 bf16-scale", "layer_packed_GBps": layer_packed / (ms * 1e-3) / 1e9,
-                   "layer_packed_frac_hbm": layer_packed / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "avg_us": dom_us, "bytes_per_launch": w13_bytes},
+                   "intermediate": wl.I, "tokens": wl.T, "topk": wl.topk, "rows": rows,
+                   "experts_touched": touched, "weights": "uint4 g32 bf16-scale",
+                   "layer_packed_GBps": layer_packed / (ms * 1e-3) / 1e9,
+                   "layer_packed_frac_hbm": layer_packed / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   "layer_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,
+                   "layer_frac_mfma": layer_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "roofline": roof,
         "kernels_avg_us": {k: v[1] / v[0] * 1e3 for k, v in kernels.items()},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wl.layout == "indexed":
         log("  timing the CPU oracle sample")
         result["cpu_baseline"] = cpu_baseline(wl, w, x, ids, tw, args.cpu_experts)
     print(json.dumps(result), flush=True)

@@ -171,6 +171,7 @@ typedef struct {
   int64_t off_offsets;  /* int32[E+1] exclusive scan of padded counts */
   int64_t off_sorted;   /* int32[cap] flat row t*topk+j, or sentinel */
   int64_t off_block_expert; /* int32[nblocks] expert of block b, -1 past total */
+  int64_t off_slot_of;  /* int32[T*topk] slot p with sorted_ids[p] = f, -1 for a dropped row */
   int64_t off_scratch;  /* internal scratch */
   int64_t total_ints;
 } moe_routing_layout_t;
@@ -184,7 +185,9 @@ moe_status_t moe_routing_layout(const moe_weights_t* h, int32_t T, int32_t topk,
  *   counts[e] = rows routed to e; offsets = exclusive scan of
  *   ceil(counts/B)*B; sorted_ids[offsets[e] + r] = r-th flat row of e in
  *   ascending t*topk+j order; all other slots hold the sentinel T*topk;
- *   block_expert[b] = expert owning block b, -1 past the total.
+ *   block_expert[b] = expert owning block b, -1 past the total;
+ *   slot_of[f] = the slot p with sorted_ids[p] = f, -1 for a row whose id
+ *   lies outside [0, E).
  *   topk_ids  device int32 [T, topk]
  *   routing   device buffer of moe_routing_bytes(h, T, topk, ovr) bytes,
  *             4-byte aligned.
@@ -212,9 +215,11 @@ moe_status_t moe_permute(const moe_weights_t* h, const uint16_t* x, int32_t T, i
  *   contiguous: rows = M_pad, topk = top-k if row_src will be passed (T via
  *               tokens), else 0
  *   masked:     rows = max_m, topk ignored
- * `tokens` is T for the combine accumulator (indexed; contiguous with
- * row_src), ignored otherwise. ovr: the indexed call's overrides (they set
- * the alignment block and so the routing capacity), NULL otherwise. */
+ * `tokens` is T when the call combines (indexed; contiguous with row_src),
+ * ignored otherwise: the workspace then holds T*topk FP32 rows of H, the
+ * routing-weighted outputs of the second GEMM that the combine sums.
+ * ovr: the indexed call's overrides (they set the alignment block and so
+ * the routing capacity), NULL otherwise. */
 size_t moe_workspace_bytes(const moe_weights_t* h, int32_t mode, int32_t rows, int32_t topk,
                            int32_t tokens, const moe_tuning_t* ovr);
 

@@ -119,6 +119,8 @@ def test_routing_layout_arithmetic(L):
     assert lay.sentinel == T * topk
     assert lay.off_counts >= 16 and lay.off_offsets >= lay.off_counts + 16
     assert lay.off_sorted >= lay.off_offsets + 17 and lay.off_block_expert >= lay.off_sorted + lay.cap
+    assert lay.off_slot_of >= lay.off_block_expert + lay.nblocks
+    assert lay.off_scratch >= lay.off_slot_of + T * topk
     assert L.moe_routing_bytes(p.h, T, topk, None) == lay.total_ints * 4
     t = M.Tuning(64, 0, 0, 0)
     assert L.moe_routing_block(p.h, T, topk, ctypes.byref(t)) == 64

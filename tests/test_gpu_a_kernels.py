@@ -57,7 +57,17 @@ def read_routing(h, routing, T, topk, ovr=None):
                 offsets=r[lay.off_offsets:lay.off_offsets + E + 1],
                 sorted_ids=r[lay.off_sorted:lay.off_sorted + lay.cap],
                 block_expert=r[lay.off_block_expert:lay.off_block_expert + lay.nblocks],
+                slot_of=r[lay.off_slot_of:lay.off_slot_of + lay.sentinel],
                 total=int(r[7]), block=lay.block)
+
+
+def slot_of_ref(al):
+    """Inverse of the oracle's sorted_ids over flat rows (-1: routed nowhere)."""
+    inv = np.full(al["sentinel"], -1, np.int32)
+    sid = al["sorted_ids"]
+    p = np.flatnonzero(sid < al["sentinel"])
+    inv[sid[p]] = p
+    return inv
 
 
 @pytest.mark.parametrize("name,E,T,topk,kind", ROUTINGS)
@@ -83,6 +93,7 @@ def test_align_bit_exact(handles, name, E, T, topk, kind, block_m):
     log(f"  align {name} B={got['block']} total={ref['total']} cap={ref['cap']}")
     for k in ("counts", "offsets", "sorted_ids", "block_expert"):
         assert np.array_equal(got[k], ref[k]), k
+    assert np.array_equal(got["slot_of"], slot_of_ref(ref))
     assert got["total"] == ref["total"]
 
 

@@ -66,7 +66,7 @@ class RoutingLayout(ctypes.Structure):
                 ("sentinel", ctypes.c_int32), ("off_header", ctypes.c_int64),
                 ("off_counts", ctypes.c_int64), ("off_offsets", ctypes.c_int64),
                 ("off_sorted", ctypes.c_int64), ("off_block_expert", ctypes.c_int64),
-                ("off_scratch", ctypes.c_int64), ("total_ints", ctypes.c_int64)]
+                ("off_slot_of", ctypes.c_int64), ("off_scratch", ctypes.c_int64), ("total_ints", ctypes.c_int64)]
 
 
 class MoeError(RuntimeError):

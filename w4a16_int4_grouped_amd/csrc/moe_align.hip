@@ -51,7 +51,8 @@ __device__ __forceinline__ uint64_t match_peers(int e) {
 // zero on exit. Called by all NWAVES*64 threads of the workgroup.
 template <int NWAVES>
 __device__ void place_rows(const int32_t* __restrict__ ids, int lo, int hi, int E,
-                           int32_t* next, int32_t* cnt, int32_t* __restrict__ sorted_ids) {
+                           int32_t* next, int32_t* cnt, int32_t* __restrict__ sorted_ids,
+                           int32_t* __restrict__ slot_of) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
@@ -71,6 +72,9 @@ __device__ void place_rows(const int32_t* __restrict__ ids, int lo, int hi, int 
       int pos = next[e] + rank;
       for (int w2 = 0; w2 < w; ++w2) pos += cnt[w2 * E + e];
       sorted_ids[pos] = f;
+      slot_of[f] = pos;
+    } else if (f < hi) {
+      slot_of[f] = -1;
     }
     __syncthreads();
     if (leader) {
@@ -108,7 +112,9 @@ __device__ void scan_experts(int32_t* padded, int32_t* offsets, int E) {
   }
 }
 
-// Sentinels in pad slots, the block -> expert map and the header.
+// Sentinels in pad slots, the block -> expert map and the header. (The
+// placement also writes slot_of[f], the slot of flat row f or -1 for a
+// dropped row, which the combine reads.)
 // start[0..E] holds the scanned offsets; counts the per-expert rows (NULL:
 // the caller has written the pad slots of each expert already).
 __device__ void fill_padding(int32_t* routing, const int32_t* start, const int32_t* counts, int E,
@@ -146,7 +152,8 @@ __global__ __launch_bounds__(1024) void align_small(const int32_t* __restrict__ 
                                                     int T, int topk, int cap, int nblocks,
                                                     int32_t* __restrict__ routing,
                                                     int64_t off_counts, int64_t off_offsets,
-                                                    int64_t off_sorted, int64_t off_be) {
+                                                    int64_t off_sorted, int64_t off_be,
+                                                    int64_t off_slot_of) {
   extern __shared__ int32_t smem[];
   int32_t* hist = smem;                  // [E + 1]: counts, then next free slot
   int32_t* start = smem + (E + 1);       // [E + 1]: padded counts, then offsets
@@ -198,10 +205,14 @@ __global__ __launch_bounds__(1024) void align_small(const int32_t* __restrict__ 
     const bool leader = e >= 0 && rank == 0;
     if (leader) cnt[w * E + e] = __popcll(peers);
     __syncthreads();
+    const int f = r * 1024 + (int)threadIdx.x;
     if (e >= 0) {
       int pos = hist[e] + rank;
       for (int w2 = 0; w2 < w; ++w2) pos += cnt[w2 * E + e];
-      sorted_ids[pos] = r * 1024 + (int)threadIdx.x;
+      sorted_ids[pos] = f;
+      routing[off_slot_of + f] = pos;
+    } else if (f < n) {
+      routing[off_slot_of + f] = -1;
     }
     __syncthreads();
     if (leader) {
@@ -263,7 +274,7 @@ template <int NWAVES>
 __global__ __launch_bounds__(NWAVES * 64) void align_scatter(const int32_t* __restrict__ ids, int n,
                                                             int E, int32_t* __restrict__ routing,
                                                             int64_t off_offsets, int64_t off_sorted,
-                                                            int64_t off_scratch) {
+                                                            int64_t off_slot_of, int64_t off_scratch) {
   extern __shared__ int32_t smem[];
   int32_t* next = smem;          // [E]
   int32_t* cnt = smem + E;       // [NWAVES][E]
@@ -274,7 +285,8 @@ __global__ __launch_bounds__(NWAVES * 64) void align_scatter(const int32_t* __re
   for (int i = threadIdx.x; i < NWAVES * E; i += NWAVES * 64) cnt[i] = 0;
   __syncthreads();
   const int lo = chunk * kAlignChunk;
-  place_rows<NWAVES>(ids, lo, min(n, lo + kAlignChunk), E, next, cnt, routing + off_sorted);
+  place_rows<NWAVES>(ids, lo, min(n, lo + kAlignChunk), E, next, cnt, routing + off_sorted,
+                     routing + off_slot_of);
 }
 
 __global__ __launch_bounds__(256) void permute_rows(const uint16_t* __restrict__ x, int topk, int H,
@@ -312,7 +324,7 @@ hipError_t launch_align(const int32_t* topk_ids, int T, int topk, int E, const R
     const size_t lds = (size_t)(2 * (E + 1) + 16 * E) * sizeof(int32_t);
     hipLaunchKernelGGL(align_small, dim3(1), dim3(1024), lds, s, topk_ids, E, L.block, T, topk, L.cap,
                        L.nblocks, routing, L.off_counts, L.off_offsets, L.off_sorted,
-                       L.off_block_expert);
+                       L.off_block_expert, L.off_slot_of);
     return hipGetLastError();
   }
   const size_t lds_e = (size_t)E * sizeof(int32_t);
@@ -326,10 +338,10 @@ hipError_t launch_align(const int32_t* topk_ids, int T, int topk, int E, const R
   if (L.nchunks > 0) {
     if (E <= 2048)   // 4 waves per chunk: 5 E ints of LDS
       hipLaunchKernelGGL(align_scatter<4>, dim3(L.nchunks), dim3(256), 5 * lds_e, s, topk_ids, n, E,
-                         routing, L.off_offsets, L.off_sorted, L.off_scratch);
+                         routing, L.off_offsets, L.off_sorted, L.off_slot_of, L.off_scratch);
     else
       hipLaunchKernelGGL(align_scatter<1>, dim3(L.nchunks), dim3(64), 2 * lds_e, s, topk_ids, n, E,
-                         routing, L.off_offsets, L.off_sorted, L.off_scratch);
+                         routing, L.off_offsets, L.off_sorted, L.off_slot_of, L.off_scratch);
   }
   return hipGetLastError();
 }

@@ -290,9 +290,11 @@ moe_status_t check_topk(const moe_weights_t* h, int T, int topk) {
   return MOE_OK;
 }
 
-// Workspace carving.
+// Workspace carving: the BF16 intermediate a, the weighted FP32 rows w*y of
+// the second GEMM (one per flat routed row, summed by the combine), the
+// contiguous layout's row-validity map, and the indexed layout's own routing.
 struct WsLayout {
-  size_t off_a = 0, off_acc = 0, off_routing = 0, total = 0;
+  size_t off_a = 0, off_y = 0, off_valid = 0, off_routing = 0, total = 0;
 };
 
 WsLayout ws_indexed(const moe_weights_t* h, int T, int topk, int block) {
@@ -302,21 +304,24 @@ WsLayout ws_indexed(const moe_weights_t* h, int T, int topk, int block) {
   size_t o = 0;
   w.off_a = o;
   o = round_up(o + (size_t)R.cap * h->desc.inter * 2, kAlign);
-  w.off_acc = o;
-  o = round_up(o + (size_t)T * h->desc.hidden * 4, kAlign);
-  w.off_routing = o;
+  w.off_y = o;
+  o = round_up(o + (size_t)T * topk * h->desc.hidden * 4, kAlign);
+  w.off_valid = w.off_routing = o;
   o = round_up(o + (size_t)R.total_ints * 4, kAlign);
   w.total = o;
   return w;
 }
 
-WsLayout ws_rows(const moe_weights_t* h, int64_t rows, int64_t acc_tokens) {
+// flat_rows: T*topk when the second GEMM feeds the combine, else 0.
+WsLayout ws_rows(const moe_weights_t* h, int64_t rows, int64_t flat_rows) {
   WsLayout w;
   size_t o = 0;
   w.off_a = o;
   o = round_up(o + (size_t)rows * h->desc.inter * 2, kAlign);
-  w.off_acc = o;
-  o = round_up(o + (size_t)acc_tokens * h->desc.hidden * 4, kAlign);
+  w.off_y = o;
+  o = round_up(o + (size_t)flat_rows * h->desc.hidden * 4, kAlign);
+  w.off_valid = w.off_routing = o;
+  o = round_up(o + (size_t)flat_rows * 4, kAlign);
   w.total = o;
   return w;
 }
@@ -469,6 +474,7 @@ moe_status_t moe_routing_layout(const moe_weights_t* h, int32_t T, int32_t topk,
   out->off_offsets = R.off_offsets;
   out->off_sorted = R.off_sorted;
   out->off_block_expert = R.off_block_expert;
+  out->off_slot_of = R.off_slot_of;
   out->off_scratch = R.off_scratch;
   out->total_ints = R.total_ints;
   return ok();
@@ -543,7 +549,7 @@ size_t moe_workspace_bytes(const moe_weights_t* h, int32_t mode, int32_t rows, i
   }
   g_err.clear();
   if (mode == MOE_MODE_MASKED) return ws_rows(h, (int64_t)h->desc.num_experts * rows, 0).total;
-  return ws_rows(h, rows, topk > 0 ? tokens : 0).total;
+  return ws_rows(h, rows, topk > 0 ? (int64_t)tokens * topk : 0).total;
 }
 
 moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32_t T, int32_t topk,
@@ -584,7 +590,7 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   }
   const int H = h->desc.hidden, I = h->desc.inter, E = h->desc.num_experts;
   uint16_t* a_ws = (uint16_t*)(wsb + W.off_a);
-  float* acc = (float*)(wsb + W.off_acc);
+  float* yrows = (float*)(wsb + W.off_y);
   GemmParams p{};
   p.counts = rt + R.off_counts;
   p.offsets = rt + R.off_offsets;
@@ -603,8 +609,6 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   p13.gather = 1;
   p13.a_out = a_ws;
   p13.a_ld = I;
-  p13.zero_ptr = acc;                    // T*H is a multiple of 4 (H % 32 == 0)
-  p13.zero_n4 = (int64_t)T * H / 4;
   if (e == hipSuccess)
     e = run("gemm_w13_small_m", s, [&] { return launch_gemm_small_m(p13, SET_INDEXED, EPI_SWIGLU, sc.nt, s); });
 
@@ -613,13 +617,15 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   p2.total_wg = E * p2.wg_per_set;
   p2.src = a_ws;
   p2.src_ld = I;
-  p2.acc_out = acc;
+  p2.yrows = yrows;
   p2.topk_w = topk_w;
-  p2.acc_ld = H;
+  p2.yrows_ld = H;
   if (e == hipSuccess)
     e = run("gemm_w2_small_m", s, [&] { return launch_gemm_small_m(p2, SET_INDEXED, EPI_COMBINE, sc.nt, s); });
   if (e == hipSuccess)
-    e = run("combine_to_bf16", s, [&] { return launch_f32_to_bf16(acc, out, (size_t)T * H, s); });
+    e = run("combine_topk", s, [&] {
+      return launch_combine_rows(yrows, rt + R.off_slot_of, rt, E, B, T, topk, H, out, s);
+    });
   if (e != hipSuccess) return hip_fail(e, "indexed launch");
   return ok();
 }
@@ -644,7 +650,7 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
   if (!aligned(a, 16) || !aligned(out, 16) || !aligned(ws, kAlign) || !aligned(m_indices, 4) ||
       (row_src && (!aligned(row_src, 4) || !aligned(topk_w, 4))))
     return fail(MOE_ERR_INVALID_ARG, "misaligned pointer (a/out 16 B, ws 256 B, others 4 B)");
-  const WsLayout W = ws_rows(h, M_pad, row_src ? T : 0);
+  const WsLayout W = ws_rows(h, M_pad, row_src ? (int64_t)T * topk : 0);
   if (ws_bytes < W.total)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu", ws_bytes, W.total);
   if ((st = set_device(h)) != MOE_OK) return st;
@@ -654,7 +660,8 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
   char* wsb = (char*)ws;
   const int H = h->desc.hidden, I = h->desc.inter;
   uint16_t* a_ws = (uint16_t*)(wsb + W.off_a);
-  float* acc = (float*)(wsb + W.off_acc);
+  float* yrows = (float*)(wsb + W.off_y);
+  int32_t* valid = (int32_t*)(wsb + W.off_valid);
   hipError_t e = hipSuccess;
 
   GemmParams p{};
@@ -672,10 +679,6 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
   p13.src_ld = H;
   p13.a_out = a_ws;
   p13.a_ld = I;
-  if (row_src && T > 0) {
-    p13.zero_ptr = acc;
-    p13.zero_n4 = (int64_t)T * H / 4;
-  }
   if (e == hipSuccess)
     e = run("gemm_w13_small_m", s, [&] { return launch_gemm_small_m(p13, SET_BLOCKS, EPI_SWIGLU, sc.nt, s); });
 
@@ -685,13 +688,19 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
   p2.src = a_ws;
   p2.src_ld = I;
   if (row_src) {
-    p2.acc_out = acc;
+    p2.yrows = yrows;
     p2.topk_w = topk_w;
-    p2.acc_ld = H;
+    p2.yrows_ld = H;
+    if (e == hipSuccess && T > 0)
+      e = run("combine_valid", s, [&] {
+        return launch_contiguous_valid(m_indices, row_src, M_pad, h->desc.num_experts, T * topk, valid, s);
+      });
     if (e == hipSuccess)
       e = run("gemm_w2_small_m", s, [&] { return launch_gemm_small_m(p2, SET_BLOCKS, EPI_COMBINE, sc.nt, s); });
     if (e == hipSuccess && T > 0)
-      e = run("combine_to_bf16", s, [&] { return launch_f32_to_bf16(acc, out, (size_t)T * H, s); });
+      e = run("combine_topk", s, [&] {
+        return launch_combine_rows(yrows, valid, nullptr, h->desc.num_experts, 0, T, topk, H, out, s);
+      });
   } else {
     p2.out = out;
     p2.out_ld = H;

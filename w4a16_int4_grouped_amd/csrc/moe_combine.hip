@@ -1,0 +1,90 @@
+// Top-k-weighted combine: out[t] = sum_j w[t, j] * y(t, j) (reading of the
+// layer's combine: the routing weight applies after the second GEMM).
+//
+// The second GEMM stores each routed row already weighted, w * y, in FP32 at
+// its flat index f = t*topk + j. This kernel adds a token's top-k rows in
+// ascending j and rounds once to BF16. No atomics: the accumulator of an
+// atomic scatter-add is shared by workgroups on all XCDs, so every add would
+// be performed past the per-XCD L2 at a fraction of the streaming rate.
+#include <hip/hip_runtime.h>
+
+#include "moe_device.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+namespace {
+
+// One thread per (token, 4 consecutive features). A row f is summed when
+// valid[f] >= 0 (the slot of f in the indexed layout's routing; 0 for the
+// contiguous layout's rows). With a routing header that does not describe
+// (E, block, T*topk) nothing was computed and the result is zero, as for the
+// GEMMs.
+__global__ __launch_bounds__(256) void combine_rows(const f32x4_t* __restrict__ yrows,
+                                                    const int32_t* __restrict__ valid,
+                                                    const int32_t* __restrict__ hdr, int E, int block,
+                                                    int T, int topk, int H4,
+                                                    u32x2_t* __restrict__ out) {
+  const int t = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T || c >= H4) return;
+  const bool ok = !hdr || (hdr[HDR_MAGIC] == kRoutingMagic && hdr[HDR_BLOCK] == block &&
+                           hdr[HDR_E] == E && hdr[HDR_T] * hdr[HDR_TOPK] == T * topk);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (ok) {
+    for (int j = 0; j < topk; ++j) {
+      const int f = t * topk + j;
+      if (valid[f] >= 0) acc += __builtin_nontemporal_load(yrows + (size_t)f * H4 + c);
+    }
+  }
+  u32x2_t r;
+  r[0] = pack_bf16x2(acc[0], acc[1]);
+  r[1] = pack_bf16x2(acc[2], acc[3]);
+  out[(size_t)t * H4 + c] = r;
+}
+
+__global__ __launch_bounds__(256) void fill_i32(int32_t* __restrict__ p, int n, int v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// One workgroup per 128-row contiguous block: the block's expert is the
+// largest valid m_index in it (as the GEMMs take it); rows of that expert
+// mark their row_src as written.
+__global__ __launch_bounds__(128) void contiguous_valid(const int32_t* __restrict__ m_indices,
+                                                        const int32_t* __restrict__ row_src, int E,
+                                                        int n_flat, int32_t* __restrict__ valid) {
+  __shared__ int32_t best;
+  const int p = blockIdx.x * 128 + threadIdx.x;
+  if (threadIdx.x == 0) best = -1;
+  __syncthreads();
+  const int m = m_indices[p];
+  if (m >= 0 && m < E) atomicMax(&best, m);
+  __syncthreads();
+  const int f = row_src[p];
+  if (m == best && best >= 0 && f >= 0 && f < n_flat) valid[f] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_combine_rows(const float* yrows, const int32_t* valid, const int32_t* hdr, int E,
+                               int block, int T, int topk, int H, uint16_t* out, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int H4 = H / 4;
+  hipLaunchKernelGGL(combine_rows, dim3((H4 + 255) / 256, T), dim3(256), 0, s,
+                     reinterpret_cast<const f32x4_t*>(yrows), valid, hdr, E, block, T, topk, H4,
+                     reinterpret_cast<u32x2_t*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_contiguous_valid(const int32_t* m_indices, const int32_t* row_src, int M_pad,
+                                   int E, int n_flat, int32_t* valid, hipStream_t s) {
+  if (n_flat > 0)
+    hipLaunchKernelGGL(fill_i32, dim3((n_flat + 255) / 256), dim3(256), 0, s, valid, n_flat, -1);
+  if (M_pad > 0)
+    hipLaunchKernelGGL(contiguous_valid, dim3(M_pad / 128), dim3(128), 0, s, m_indices, row_src, E,
+                       n_flat, valid);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -30,8 +30,9 @@
 //
 // Epilogues: SwiGLU into the BF16 intermediate (W13, gate/up tiles
 // interleaved so both halves of a column sit in the same lane and register),
-// FP32 top-k-weighted scatter-add (W2, indexed / contiguous with row_src), or
-// a BF16 store (W2, masked / contiguous without row_src).
+// the routing-weighted FP32 row w*y stored at its flat index for the combine
+// kernel (W2, indexed / contiguous with row_src), or a BF16 store (W2,
+// masked / contiguous without row_src).
 #include <hip/hip_runtime.h>
 
 #include "moe_device.h"
@@ -121,13 +122,6 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
   __shared__ TileLds<NT> lds;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-  if (p.zero_ptr) {   // clear the combine accumulator the next GEMM adds into
-    const int64_t per = (p.zero_n4 + p.total_wg - 1) / p.total_wg;
-    const int64_t lo = (int64_t)blockIdx.x * per;
-    const int64_t hi = min(lo + per, p.zero_n4);
-    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) reinterpret_cast<f32x4_t*>(p.zero_ptr)[i] = z;
-  }
   const int logical = xcd_remap(blockIdx.x, p.total_wg);
   const int set = logical / p.wg_per_set;
   const int rg_raw = (logical - set * p.wg_per_set) * 4 + wave;
@@ -248,14 +242,11 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
         }
         if (f < 0 || f >= p.sentinel) continue;
         const float w = p.topk_w[f];
-        float* dst = p.acc_out + (size_t)(f / p.topk) * p.acc_ld;
+        float* dst = p.yrows + (size_t)f * p.yrows_ld;
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
           const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
-          if (n < p.N) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + n + i, w * acc[mt][nt][i]);
-          }
+          if (n < p.N) *reinterpret_cast<f32x4_t*>(dst + n) = w * acc[mt][nt];
         }
       } else {
         uint16_t* dst = p.out + (size_t)slot * p.out_ld;

@@ -18,7 +18,7 @@ enum RowSet : int {
 // What the GEMM does with its FP32 tile.
 enum Epilogue : int {
   EPI_SWIGLU = 0,    // W13: a[slot][c] = bf16(silu(gate) * up)
-  EPI_COMBINE = 1,   // W2: acc[t][n] += w[f] * y   (f from sorted_ids / row_src)
+  EPI_COMBINE = 1,   // W2: yrows[f][n] = w[f] * y   (f from sorted_ids / row_src)
   EPI_STORE = 2,     // W2: out[slot][n] = bf16(y)
 };
 
@@ -48,15 +48,11 @@ struct GemmParams {
   // epilogue targets
   uint16_t* a_out;
   int64_t a_ld;               // SWIGLU
-  float* acc_out;
+  float* yrows;
   const float* topk_w;
-  int64_t acc_ld;             // COMBINE
+  int64_t yrows_ld;           // COMBINE: weighted rows, one per flat index f
   uint16_t* out;
   int64_t out_ld;             // STORE
-  // optional: float4 words cleared by the kernel's workgroups before their
-  // tiles (the accumulator of a following COMBINE GEMM)
-  float* zero_ptr;
-  int64_t zero_n4;
 };
 
 hipError_t launch_gemm_small_m(const GemmParams& p, int set, int epi, int nt, hipStream_t s);
@@ -70,8 +66,15 @@ hipError_t launch_repack(const MatLayout& m, const int32_t* words, const uint16_
                          char* prepared, int32_t* bad_scale_flag, hipStream_t s);
 hipError_t launch_dequant_expert(const MatLayout& m, const char* prepared, int expert,
                                  uint16_t* out, hipStream_t s);
-hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t s);
-hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s);
+// out[t] = bf16(sum over j ascending of yrows[t*topk + j]) for rows with
+// valid[t*topk + j] >= 0; tokens with no such row get 0. hdr (may be NULL):
+// routing header that must describe (E, block, T*topk), else out = 0.
+hipError_t launch_combine_rows(const float* yrows, const int32_t* valid, const int32_t* hdr, int E,
+                               int block, int T, int topk, int H, uint16_t* out, hipStream_t s);
+// valid[f] = 0 for every f = row_src[p] of a non-padding contiguous row (the
+// block's expert, as the GEMMs take it), -1 for every other f < T*topk.
+hipError_t launch_contiguous_valid(const int32_t* m_indices, const int32_t* row_src, int M_pad,
+                                   int E, int n_flat, int32_t* valid, hipStream_t s);
 
 }  // namespace moe

@@ -76,7 +76,7 @@ constexpr int32_t kRoutingMagic = 0x31414F4D;
 struct RoutingLayout {
   int32_t block = 0, cap = 0, nblocks = 0, sentinel = 0, nchunks = 0;
   int64_t off_header = 0, off_counts = 0, off_offsets = 0, off_sorted = 0,
-          off_block_expert = 0, off_scratch = 0, total_ints = 0;
+          off_block_expert = 0, off_slot_of = 0, off_scratch = 0, total_ints = 0;
   void init(int E, int T, int topk, int B) {
     block = B;
     sentinel = T * topk;
@@ -89,7 +89,8 @@ struct RoutingLayout {
     off_offsets = r64(off_counts + E);
     off_sorted = r64(off_offsets + E + 1);
     off_block_expert = r64(off_sorted + cap);
-    off_scratch = r64(off_block_expert + nblocks);
+    off_slot_of = r64(off_block_expert + nblocks);
+    off_scratch = r64(off_slot_of + sentinel);
     total_ints = r64(off_scratch + (int64_t)(nchunks > 0 ? nchunks : 1) * E);
   }
 };

@@ -100,17 +100,6 @@ __global__ __launch_bounds__(256) void zero_tail(uint32_t* __restrict__ p, size_
   if (i < n) p[i] = 0u;
 }
 
-__global__ __launch_bounds__(256) void f32_to_bf16_x4(const f32x4_t* __restrict__ in,
-                                                      u32x2_t* __restrict__ out, size_t n4) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-    const f32x4_t v = in[i];
-    u32x2_t r;
-    r[0] = pack_bf16x2(v[0], v[1]);
-    r[1] = pack_bf16x2(v[2], v[3]);
-    out[i] = r;
-  }
-}
-
 inline unsigned grid_for(size_t n, size_t per_block, unsigned cap) {
   size_t g = (n + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -151,21 +140,8 @@ hipError_t launch_dequant_expert(const MatLayout& m, const char* prepared, int e
   return hipGetLastError();
 }
 
-hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s) {
-  return zero_words(reinterpret_cast<uint32_t*>(p), n, s);
-}
-
 hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t s) {
   return zero_words(reinterpret_cast<uint32_t*>(p), n, s);
-}
-
-// n must be a multiple of 4 (rows of H elements, H a multiple of 32).
-hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, size_t n, hipStream_t s) {
-  const size_t n4 = n / 4;
-  if (n4 == 0) return hipSuccess;
-  hipLaunchKernelGGL(f32_to_bf16_x4, dim3(grid_for(n4, 256, 8192)), dim3(256), 0, s,
-                     reinterpret_cast<const f32x4_t*>(in), reinterpret_cast<u32x2_t*>(out), n4);
-  return hipGetLastError();
 }
 
 }  // namespace moe
