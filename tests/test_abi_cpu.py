@@ -214,3 +214,27 @@ def test_describe_reports_schedule(L):
 def test_status_strings(L):
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(4) == b"MOE_ERR_OVERRIDE_REJECTED"
+
+
+def test_schedule_choice_by_rows_per_expert(L):
+    """Indexed: below 80 rows per expert small-M with 16-row alignment, at
+    or above it large-M with 128-row blocks (tokens per expert, not total
+    tokens, decide); an explicit large-M request the kernel cannot serve is
+    rejected."""
+    p = Plan(L, "indexed", E=16, H=256, I=128)
+    assert L.moe_routing_block(p.h, 100, 4, None) == 16        # 25 rows / expert
+    assert L.moe_routing_block(p.h, 320, 4, None) == 128       # 80 rows / expert
+    small = M.Tuning(0, 1, 0, 0)
+    assert L.moe_routing_block(p.h, 320, 4, ctypes.byref(small)) == 16
+    large = M.Tuning(0, 2, 0, 0)
+    assert L.moe_routing_block(p.h, 8, 2, ctypes.byref(large)) == 128
+    large64 = M.Tuning(64, 2, 0, 0)
+    assert L.moe_routing_block(p.h, 320, 4, ctypes.byref(large64)) == 0
+    assert "large-M" in M.last_error()
+    tail = Plan(L, "indexed", E=16, H=160, I=96)               # K not whole 128-chunks
+    assert L.moe_routing_block(tail.h, 320, 4, None) == 16
+    assert L.moe_routing_block(tail.h, 320, 4, ctypes.byref(large)) == 0
+    fake = ctypes.c_void_p(1 << 20)
+    st = L.moe_w4a16_indexed(tail.h, fake, 320, 4, fake, fake, None, fake, fake, 1 << 40,
+                             ctypes.byref(large), None)
+    assert st == M.MOE_ERR_OVERRIDE_REJECTED

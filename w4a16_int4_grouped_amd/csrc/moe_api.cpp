@@ -159,6 +159,16 @@ struct Schedule {
   int rows = 0;     // rows per expert the choice was made for
 };
 
+// Launches one GEMM (mat 13 or 2) with the schedule's kernel, timed under a
+// fixed name.
+hipError_t run_gemm(int mat, const Schedule& sc, const GemmParams& p, int set, int epi, hipStream_t s) {
+  if (sc.kind == SCHED_LARGE_M)
+    return run(mat == 13 ? "gemm_w13_large_m" : "gemm_w2_large_m", s,
+               [&] { return launch_gemm_large_m(p, set, epi, s); });
+  return run(mat == 13 ? "gemm_w13_small_m" : "gemm_w2_small_m", s,
+             [&] { return launch_gemm_small_m(p, set, epi, sc.nt, s); });
+}
+
 int nt_for_rows(int rows) {
   if (rows <= 16) return 1;
   if (rows <= 32) return 2;
@@ -193,6 +203,23 @@ uint64_t key_of(int mode, int a, int b, const moe_tuning_t* o) {
 
 // Indexed: rows per expert tok_e = ceil(T*topk / E) picks the schedule (the
 // Chord page's tok_e rule: tokens per expert, not total tokens).
+// The large-M kernel works on whole K chunks of 128 (both GEMMs).
+bool large_m_fits(const moe_weights* h) {
+  return h->desc.hidden % kKC == 0 && h->desc.inter % kKC == 0;
+}
+
+const char* kind_name(int kind) { return kind == SCHED_LARGE_M ? "large-M" : "small-M"; }
+
+// An explicit large-M request the kernel cannot serve (K not whole chunks,
+// or an alignment block other than its 128-row tile).
+bool large_m_rejected(const moe_weights* h, const moe_tuning_t* ovr) {
+  return ovr && ovr->schedule == SCHED_LARGE_M &&
+         (!large_m_fits(h) || (ovr->block_m && ovr->block_m != 128));
+}
+
+// Indexed: rows per expert tok_e = ceil(T*topk / E) picks the schedule (the
+// Chord page's tok_e rule: tokens per expert, not total tokens). Large-M
+// aligns each expert to 128-row blocks, its token tile.
 Schedule schedule_indexed(moe_weights* h, int T, int topk, const moe_tuning_t* ovr) {
   const uint64_t key = key_of(MOE_MODE_INDEXED, T, topk, ovr);
   std::lock_guard<std::mutex> g(h->mu);
@@ -204,17 +231,16 @@ Schedule schedule_indexed(moe_weights* h, int T, int topk, const moe_tuning_t* o
   s.rows = (int)rows;
   s.kind = rows < kLargeMRows ? SCHED_SMALL_M : SCHED_LARGE_M;
   if (h->env.schedule) s.kind = h->env.schedule;
+  if (ovr && ovr->block_m && ovr->block_m != 128) s.kind = SCHED_SMALL_M;
   if (ovr && ovr->schedule) s.kind = ovr->schedule;
-  // The large-M kernel is not built yet: every indexed call runs small-M with
-  // tiles covering the expected rows.
-  s.kind = SCHED_SMALL_M;
+  if (!large_m_fits(h)) s.kind = SCHED_SMALL_M;
   s.nt = nt_for_rows((int)rows);
   if (h->env.nt) s.nt = h->env.nt;
-  s.block = 16;
+  s.block = s.kind == SCHED_LARGE_M ? 128 : 16;
   if (ovr && ovr->block_m) s.block = ovr->block_m;
   if (h->env.log)
-    std::fprintf(stderr, "[moe_w4a16] indexed T=%d topk=%d rows/expert=%ld -> small-M nt=%d block=%d\n",
-                 T, topk, rows, s.nt, s.block);
+    std::fprintf(stderr, "[moe_w4a16] indexed T=%d topk=%d rows/expert=%ld -> %s nt=%d block=%d\n",
+                 T, topk, rows, kind_name(s.kind), s.nt, s.block);
   h->cache.emplace(key, s);
   return s;
 }
@@ -226,17 +252,22 @@ Schedule schedule_masked(moe_weights* h, int max_m, int expected_m) {
   if (it != h->cache.end()) return it->second;
   Schedule s;
   s.rows = expected_m;
-  // The row budget bounds every expert's rows: cover it in one weight pass
-  // when it fits four token tiles.
+  s.kind = expected_m < kLargeMRows ? SCHED_SMALL_M : SCHED_LARGE_M;
+  if (h->env.schedule) s.kind = h->env.schedule;
+  if (!large_m_fits(h)) s.kind = SCHED_SMALL_M;
+  // Small-M: the row budget bounds every expert's rows; cover it in one
+  // weight pass when it fits four token tiles.
   s.nt = nt_for_rows(max_m < 64 ? max_m : 64);
   if (h->env.nt) s.nt = h->env.nt;
   if (h->env.log)
-    std::fprintf(stderr, "[moe_w4a16] masked max_m=%d expected_m=%d -> small-M nt=%d\n", max_m,
-                 expected_m, s.nt);
+    std::fprintf(stderr, "[moe_w4a16] masked max_m=%d expected_m=%d -> %s nt=%d\n", max_m,
+                 expected_m, kind_name(s.kind), s.nt);
   h->cache.emplace(key, s);
   return s;
 }
 
+// Contiguous: every block is a full 128-row tile, which the large-M kernel
+// covers in one weight pass.
 Schedule schedule_contiguous(moe_weights* h, int M_pad) {
   const uint64_t key = key_of(MOE_MODE_CONTIGUOUS, M_pad, 0, nullptr);
   std::lock_guard<std::mutex> g(h->mu);
@@ -244,6 +275,9 @@ Schedule schedule_contiguous(moe_weights* h, int M_pad) {
   if (it != h->cache.end()) return it->second;
   Schedule s;
   s.rows = 128;
+  s.kind = SCHED_LARGE_M;
+  if (h->env.schedule) s.kind = h->env.schedule;
+  if (!large_m_fits(h)) s.kind = SCHED_SMALL_M;
   s.nt = 2;
   if (h->env.nt) s.nt = h->env.nt;
   h->cache.emplace(key, s);
@@ -453,6 +487,12 @@ int32_t moe_routing_block(const moe_weights_t* h, int32_t T, int32_t topk, const
     fail(MOE_ERR_INVALID_ARG, "block_m %d not in {16, 32, 64, 128}", ovr->block_m);
     return 0;
   }
+  if (large_m_rejected(h, ovr)) {
+    fail(MOE_ERR_OVERRIDE_REJECTED,
+         "large-M needs hidden and inter divisible by 128 and block_m 0 or 128 (got H=%d I=%d block_m=%d)",
+         h->desc.hidden, h->desc.inter, ovr->block_m);
+    return 0;
+  }
   g_err.clear();
   return schedule_indexed(const_cast<moe_weights_t*>(h), T, topk, ovr).block;
 }
@@ -563,7 +603,7 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   if (ovr && ovr->schedule && (ovr->schedule < 0 || ovr->schedule > 2))
     return fail(MOE_ERR_INVALID_ARG, "schedule override %d not in 0..2", ovr->schedule);
   const int B = moe_routing_block(h, T, topk, ovr);
-  if (!B) return MOE_ERR_INVALID_ARG;
+  if (!B) return large_m_rejected(h, ovr) ? MOE_ERR_OVERRIDE_REJECTED : MOE_ERR_INVALID_ARG;
   if (T == 0) return ok();
   if (!x || !topk_w || !out || !ws || (!routing && !topk_ids))
     return fail(MOE_ERR_INVALID_ARG, "NULL x / topk_w / out / ws / topk_ids");
@@ -599,29 +639,33 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   p.sentinel = T * topk;
   p.topk = topk;
   p.block = B;
-  p.nsets = E;
+  p.block_expert = rt + R.off_block_expert;
+  // small-M: one row set per expert; large-M: one per 128-slot routing block
+  const bool large = sc.kind == SCHED_LARGE_M;
+  p.nsets = large ? R.nblocks : E;
+  const int set = large ? SET_ROUTED : SET_INDEXED;
 
   GemmParams p13 = p;
   fill_weights(p13, h, h->lay.w13);
-  p13.total_wg = E * p13.wg_per_set;
+  p13.total_wg = p13.nsets * p13.wg_per_set;
   p13.src = x;
   p13.src_ld = H;
   p13.gather = 1;
   p13.a_out = a_ws;
   p13.a_ld = I;
   if (e == hipSuccess)
-    e = run("gemm_w13_small_m", s, [&] { return launch_gemm_small_m(p13, SET_INDEXED, EPI_SWIGLU, sc.nt, s); });
+    e = run_gemm(13, sc, p13, set, EPI_SWIGLU, s);
 
   GemmParams p2 = p;
   fill_weights(p2, h, h->lay.w2);
-  p2.total_wg = E * p2.wg_per_set;
+  p2.total_wg = p2.nsets * p2.wg_per_set;
   p2.src = a_ws;
   p2.src_ld = I;
   p2.yrows = yrows;
   p2.topk_w = topk_w;
   p2.yrows_ld = H;
   if (e == hipSuccess)
-    e = run("gemm_w2_small_m", s, [&] { return launch_gemm_small_m(p2, SET_INDEXED, EPI_COMBINE, sc.nt, s); });
+    e = run_gemm(2, sc, p2, set, EPI_COMBINE, s);
   if (e == hipSuccess)
     e = run("combine_topk", s, [&] {
       return launch_combine_rows(yrows, rt + R.off_slot_of, rt, E, B, T, topk, H, out, s);
@@ -680,7 +724,7 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
   p13.a_out = a_ws;
   p13.a_ld = I;
   if (e == hipSuccess)
-    e = run("gemm_w13_small_m", s, [&] { return launch_gemm_small_m(p13, SET_BLOCKS, EPI_SWIGLU, sc.nt, s); });
+    e = run_gemm(13, sc, p13, SET_BLOCKS, EPI_SWIGLU, s);
 
   GemmParams p2 = p;
   fill_weights(p2, h, h->lay.w2);
@@ -696,7 +740,7 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
         return launch_contiguous_valid(m_indices, row_src, M_pad, h->desc.num_experts, T * topk, valid, s);
       });
     if (e == hipSuccess)
-      e = run("gemm_w2_small_m", s, [&] { return launch_gemm_small_m(p2, SET_BLOCKS, EPI_COMBINE, sc.nt, s); });
+      e = run_gemm(2, sc, p2, SET_BLOCKS, EPI_COMBINE, s);
     if (e == hipSuccess && T > 0)
       e = run("combine_topk", s, [&] {
         return launch_combine_rows(yrows, valid, nullptr, h->desc.num_experts, 0, T, topk, H, out, s);
@@ -705,7 +749,7 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
     p2.out = out;
     p2.out_ld = H;
     if (e == hipSuccess)
-      e = run("gemm_w2_small_m", s, [&] { return launch_gemm_small_m(p2, SET_BLOCKS, EPI_STORE, sc.nt, s); });
+      e = run_gemm(2, sc, p2, SET_BLOCKS, EPI_STORE, s);
   }
   if (e != hipSuccess) return hip_fail(e, "contiguous launch");
   return ok();
@@ -750,7 +794,7 @@ moe_status_t moe_w4a16_masked(const moe_weights_t* hc, const uint16_t* a3, int32
   p13.src_ld = H;
   p13.a_out = a_ws;
   p13.a_ld = I;
-  hipError_t e = run("gemm_w13_small_m", s, [&] { return launch_gemm_small_m(p13, SET_MASKED, EPI_SWIGLU, sc.nt, s); });
+  hipError_t e = run_gemm(13, sc, p13, SET_MASKED, EPI_SWIGLU, s);
 
   GemmParams p2 = p;
   fill_weights(p2, h, h->lay.w2);
@@ -760,7 +804,7 @@ moe_status_t moe_w4a16_masked(const moe_weights_t* hc, const uint16_t* a3, int32
   p2.out = out;
   p2.out_ld = H;
   if (e == hipSuccess)
-    e = run("gemm_w2_small_m", s, [&] { return launch_gemm_small_m(p2, SET_MASKED, EPI_STORE, sc.nt, s); });
+    e = run_gemm(2, sc, p2, SET_MASKED, EPI_STORE, s);
   if (e != hipSuccess) return hip_fail(e, "masked launch");
   return ok();
 }
@@ -790,23 +834,27 @@ int moe_describe(const moe_weights_t* hc, int32_t mode, int32_t rows, int32_t to
   int len = -1;
   if (mode == MOE_MODE_INDEXED) {
     if (check_topk(h, rows, topk) != MOE_OK) return -1;
+    if (large_m_rejected(h, ovr)) return -1;
     const Schedule s = schedule_indexed(h, rows, topk, ovr);
+    RoutingLayout R;
+    R.init(E, rows, topk, s.block);
+    const int sets = s.kind == SCHED_LARGE_M ? R.nblocks : E;
     len = std::snprintf(buf, n,
-                        "layout=indexed T=%d topk=%d rows_per_expert=%d schedule=small-M block=%d nt=%d "
+                        "layout=indexed T=%d topk=%d rows_per_expert=%d schedule=%s block=%d nt=%d "
                         "grid_w13=%d grid_w2=%d",
-                        rows, topk, s.rows, s.block, s.nt, E * wg13, E * wg2);
+                        rows, topk, s.rows, kind_name(s.kind), s.block, s.nt, sets * wg13, sets * wg2);
   } else if (mode == MOE_MODE_MASKED) {
     if (expected_m <= 0 || rows < 0) return -1;
     const Schedule s = schedule_masked(h, rows, expected_m);
     len = std::snprintf(buf, n,
-                        "layout=masked max_m=%d expected_m=%d schedule=small-M nt=%d grid_w13=%d grid_w2=%d",
-                        rows, expected_m, s.nt, E * wg13, E * wg2);
+                        "layout=masked max_m=%d expected_m=%d schedule=%s nt=%d grid_w13=%d grid_w2=%d",
+                        rows, expected_m, kind_name(s.kind), s.nt, E * wg13, E * wg2);
   } else {
     if (rows < 0 || rows % 128) return -1;
     const Schedule s = schedule_contiguous(h, rows);
     len = std::snprintf(buf, n,
-                        "layout=contiguous M_pad=%d blocks=%d schedule=small-M nt=%d grid_w13=%d grid_w2=%d",
-                        rows, rows / 128, s.nt, (rows / 128) * wg13, (rows / 128) * wg2);
+                        "layout=contiguous M_pad=%d blocks=%d schedule=%s nt=%d grid_w13=%d grid_w2=%d",
+                        rows, rows / 128, kind_name(s.kind), s.nt, (rows / 128) * wg13, (rows / 128) * wg2);
   }
   if (len < 0) return -1;
   return len < (int)n ? len : (int)n - 1;

@@ -1,0 +1,281 @@
+// Grouped W4A16 GEMM, large-M schedule (many rows per expert).
+//
+// Above roughly 80 rows per expert the GEMM is a dense contraction and the
+// tile follows each expert's padded rows (Chord page, "Indexed kernels",
+// Fig. 2, and "H200 prefill and TP8": block_m sized to the padded rows).
+//
+// Work item: one 128-row token tile x 256 weight rows. The four waves each
+// own one row group of 64 weight rows (4 MFMA tiles of 16 rows) and all 128
+// tokens (8 MFMA tiles of 16 columns), so a wave holds 4 x 8 accumulator
+// tiles. Weights stay on the A side of v_mfma_f32_16x16x32_bf16 as in the
+// small-M kernel and use the same prepared layout: a lane's 32 k values of a
+// tile share one scale group, so a dequantised A fragment (17 VALU
+// instructions for 8 weights) feeds eight MFMAs, and VALU work stays near
+// half of the MFMA time.
+//
+// Per K chunk of 128:
+//   * the token tile (128 rows x 128 k of BF16, 32 KB) goes straight from
+//     global memory to LDS (global_load_lds_dwordx4, no staging registers),
+//     one chunk ahead, into the other of two buffers;
+//   * each wave loads its 4 KB of packed weights and 512 B of scales one
+//     chunk ahead into registers;
+//   * both are issued at the top of the chunk, so the barrier at its end
+//     (which waits for every outstanding load) finds them long arrived.
+// LDS layout of a buffer: blocks of 1 KB, block (q, s) holding rows
+// [16q, 16q+16) x 16-byte k pieces [4s, 4s+4); row rr of a block keeps its
+// 4 pieces in 64 B with piece p at position p ^ swz(rr). The swizzle makes
+// every MFMA B-fragment read (16 rows, one piece each) hit distinct banks,
+// whether the LDS serves 8 or 16 lanes of a 16-byte read per cycle.
+//
+// Row sets: a 128-slot block of the indexed routing (block 128; rows via
+// sorted_ids, pad slots hold the sentinel), a 128-row block of the
+// contiguous layout, or an expert of the masked layout (tiles of 128 over
+// its valid rows). Epilogues as in the small-M kernel.
+#include <hip/hip_runtime.h>
+
+#include "moe_device.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBM = 128;                       // token rows per tile
+constexpr int kBufU4 = kBM * kKC * 2 / 16;     // 16-byte slots per LDS buffer (2048)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ int swz(int rr) { return ((rr >> 1) ^ (rr >> 2)) & 3; }
+
+struct AFragL {
+  u32x4_t A[kMT];
+  u32x2_t S;
+};
+
+__device__ __forceinline__ void load_a_l(AFragL& f, const u32x4_t* __restrict__ wq,
+                                         const u32x2_t* __restrict__ ws, int lane) {
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) f.A[mt] = __builtin_nontemporal_load(wq + mt * 64 + lane);
+  f.S = __builtin_nontemporal_load(ws + lane);
+}
+
+// This wave's share of the token tile of one chunk: row blocks 2w and 2w+1,
+// all four piece groups (8 x 1 KB). src0/src1: the lane's row pointers (with
+// its swizzled piece offset) at chunk 0.
+__device__ __forceinline__ void dma_tile(u32x4_t* lds_buf, const char* src0, const char* src1,
+                                         int kc, int wave) {
+#pragma unroll
+  for (int ql = 0; ql < 2; ++ql) {
+    const char* src = (ql ? src1 : src0) + (size_t)kc * (kKC * 2);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t* dst = lds_buf + ((2 * wave + ql) * 4 + s) * 64;
+      __builtin_amdgcn_global_load_lds(src + s * 64, (lds_void_t*)dst, 16, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void mma_chunk_l(const AFragL& f, const u32x4_t* lds_buf, const int (&rd)[4],
+                                            f32x4_t (&acc)[kMT][8], uint32_t magic) {
+  GroupScale gs[kMT];
+  {
+    const float sc[4] = {bf16_lo(f.S[0]), bf16_hi(f.S[0]), bf16_lo(f.S[1]), bf16_hi(f.S[1])};
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) gs[mt] = group_scale(sc[mt]);
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    u32x4_t a[kMT];
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) a[mt] = dq8(f.A[mt][g], gs[mt], magic);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const u32x4_t b = lds_buf[rd[g] + nt * 256];
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) acc[mt][nt] = mfma16(a[mt], b, acc[mt][nt]);
+    }
+  }
+}
+
+template <int SET, int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_large_m(const GemmParams p) {
+  constexpr bool kGather = (SET == SET_ROUTED && EPI == EPI_SWIGLU);
+  __shared__ u32x4_t lds[2][kBufU4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int logical = xcd_remap(blockIdx.x, p.total_wg);
+  const int set = logical / p.wg_per_set;
+  const int rg_raw = (logical - set * p.wg_per_set) * 4 + wave;
+  const bool active = rg_raw < p.RG;
+  const int rg = active ? rg_raw : p.RG - 1;
+
+  // ---- the row set (uniform over the workgroup)
+  int e, slot0, count;
+  if constexpr (SET == SET_ROUTED) {
+    const int32_t* hdr = p.routing_hdr;
+    if (hdr[HDR_MAGIC] != kRoutingMagic || hdr[HDR_BLOCK] != p.block || hdr[HDR_E] != p.E ||
+        hdr[HDR_T] * hdr[HDR_TOPK] != p.sentinel)
+      return;
+    e = p.block_expert[set];
+    slot0 = set * kBM;
+    count = kBM;
+  } else if constexpr (SET == SET_MASKED) {
+    e = set;
+    slot0 = e * p.max_m;
+    count = min(max(p.masked_m[e], 0), p.max_m);
+  } else {
+    slot0 = set * p.block_rows;
+    count = p.block_rows;
+    int m = -1;
+    for (int r = lane; r < p.block_rows; r += 64) {
+      const int v = p.m_indices[slot0 + r];
+      if (v >= 0 && v < p.E) m = max(m, v);
+    }
+    e = wave_max(m);
+  }
+  if (count <= 0 || e < 0 || e >= p.E) return;
+
+  const size_t tile0 = ((size_t)e * p.RG + rg) * p.Kc;
+  const u32x4_t* __restrict__ wq = reinterpret_cast<const u32x4_t*>(p.wq) + tile0 * (kMT * 64);
+  const u32x2_t* __restrict__ ws = reinterpret_cast<const u32x2_t*>(p.wsc) + tile0 * 64;
+  const int Kc = p.Kc;
+  const uint32_t magic = kF16Magic;
+
+  // B-fragment read offsets (16-byte slots) for the 4 MFMA steps of a chunk:
+  // row (lane & 15) of row block nt, piece 4*(lane >> 4) + g.
+  int rd[4];
+  {
+    const int rr = lane & 15;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) rd[g] = (lane >> 4) * 64 + rr * 4 + (g ^ swz(rr));
+  }
+  // DMA source: this lane writes row 16*q + (lane >> 2) of a row block, in
+  // position (lane & 3), which holds piece (lane & 3) ^ swz(lane >> 2).
+  const int dma_piece = ((lane & 3) ^ swz(lane >> 2)) * 16;
+
+  for (int tb = 0; tb < count; tb += kBM) {
+    const char* src[2];
+#pragma unroll
+    for (int ql = 0; ql < 2; ++ql) {
+      const int r = tb + 32 * wave + 16 * ql + (lane >> 2);   // tile row
+      int row;
+      if constexpr (SET == SET_ROUTED) {
+        if constexpr (kGather) {
+          const int f = p.sorted_ids[slot0 + r];
+          row = (f >= 0 && f < p.sentinel) ? f / p.topk : 0;   // pad slots read row 0
+        } else {
+          row = slot0 + r;
+        }
+      } else if constexpr (SET == SET_MASKED) {
+        row = slot0 + min(r, count - 1);   // pad rows repeat a valid row
+      } else {
+        row = slot0 + r;
+      }
+      src[ql] = reinterpret_cast<const char*>(p.src + (size_t)row * p.src_ld) + dma_piece;
+    }
+
+    f32x4_t acc[kMT][8];
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    AFragL fa, fb;
+    __syncthreads();   // the previous tile's readers are done with buffer 0
+    dma_tile(lds[0], src[0], src[1], 0, wave);
+    load_a_l(fa, wq, ws, lane);
+    __syncthreads();
+
+    // step: compute chunk c from (CUR, buffer BUF); chunk c+1 is fetched into
+    // (NXT, the other buffer) first.
+#define MOE_LARGE_M_STEP(BUF, CUR, NXT, C)                                                    \
+  if ((C) < Kc) {                                                                             \
+    if ((C) + 1 < Kc) {                                                                       \
+      dma_tile(lds[(BUF) ^ 1], src[0], src[1], (C) + 1, wave);                                \
+      load_a_l(NXT, wq + (size_t)((C) + 1) * (kMT * 64), ws + (size_t)((C) + 1) * 64, lane);  \
+    }                                                                                         \
+    mma_chunk_l(CUR, lds[BUF], rd, acc, magic);                                               \
+    __syncthreads();                                                                          \
+  }
+    for (int kc = 0; kc < Kc; kc += 2) {
+      MOE_LARGE_M_STEP(0, fa, fb, kc)
+      MOE_LARGE_M_STEP(1, fb, fa, kc + 1)
+    }
+#undef MOE_LARGE_M_STEP
+    if (!active) continue;
+
+    // ---- epilogue
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const int r = tb + nt * 16 + (lane & 15);
+      if (r >= count) continue;
+      const int slot = slot0 + r;
+      if constexpr (EPI == EPI_SWIGLU) {
+        if constexpr (SET == SET_ROUTED) {
+          const int f = p.sorted_ids[slot];
+          if (f < 0 || f >= p.sentinel) continue;   // pad slot: never read back
+        }
+        uint16_t* dst = p.a_out + (size_t)slot * p.a_ld + rg * 32 + (lane >> 4) * 4;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const f32x4_t g = acc[2 * pp][nt], u = acc[2 * pp + 1][nt];
+          u32x2_t v;
+          v[0] = pack_bf16x2(swiglu(g[0], u[0]), swiglu(g[1], u[1]));
+          v[1] = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
+          *reinterpret_cast<u32x2_t*>(dst + pp * 16) = v;
+        }
+      } else if constexpr (EPI == EPI_COMBINE) {
+        int f;
+        if constexpr (SET == SET_ROUTED) {
+          f = p.sorted_ids[slot];
+        } else {
+          f = (p.m_indices[slot] == e) ? p.row_src[slot] : -1;
+        }
+        if (f < 0 || f >= p.sentinel) continue;
+        const float w = p.topk_w[f];
+        float* dst = p.yrows + (size_t)f * p.yrows_ld;
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+          const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
+          if (n < p.N) *reinterpret_cast<f32x4_t*>(dst + n) = w * acc[mt][nt];
+        }
+      } else {
+        uint16_t* dst = p.out + (size_t)slot * p.out_ld;
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+          const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
+          if (n < p.N) {
+            u32x2_t v;
+            v[0] = pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]);
+            v[1] = pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]);
+            *reinterpret_cast<u32x2_t*>(dst + n) = v;
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_large_m(const GemmParams& p, int set, int epi, hipStream_t s) {
+  if (p.total_wg <= 0) return hipSuccess;
+  if (p.K % kKC) return hipErrorInvalidValue;   // whole chunks only
+  const dim3 grid(p.total_wg), block(256);
+#define MOE_GEMM_CASE(SET_, EPI_)                                                  \
+  if (set == SET_ && epi == EPI_) {                                                \
+    hipLaunchKernelGGL((gemm_large_m<SET_, EPI_>), grid, block, 0, s, p);         \
+    return hipGetLastError();                                                      \
+  }
+  MOE_GEMM_CASE(SET_ROUTED, EPI_SWIGLU)
+  MOE_GEMM_CASE(SET_ROUTED, EPI_COMBINE)
+  MOE_GEMM_CASE(SET_MASKED, EPI_SWIGLU)
+  MOE_GEMM_CASE(SET_MASKED, EPI_STORE)
+  MOE_GEMM_CASE(SET_BLOCKS, EPI_SWIGLU)
+  MOE_GEMM_CASE(SET_BLOCKS, EPI_COMBINE)
+  MOE_GEMM_CASE(SET_BLOCKS, EPI_STORE)
+#undef MOE_GEMM_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -13,6 +13,7 @@ enum RowSet : int {
   SET_INDEXED = 0,   // expert e: slots offsets[e] .. + counts[e]
   SET_MASKED = 1,    // expert e: slots e*max_m .. + clamp(masked_m[e])
   SET_BLOCKS = 2,    // block b of block_rows slots; expert from m_indices
+  SET_ROUTED = 3,    // block b of the indexed routing (block 128); expert block_expert[b]
 };
 
 // What the GEMM does with its FP32 tile.
@@ -35,6 +36,7 @@ struct GemmParams {
   const int32_t* offsets;
   const int32_t* sorted_ids;
   const int32_t* routing_hdr;
+  const int32_t* block_expert;
   int sentinel, topk, block;  // indexed
   const int32_t* masked_m;
   int max_m;                  // masked
@@ -56,6 +58,8 @@ struct GemmParams {
 };
 
 hipError_t launch_gemm_small_m(const GemmParams& p, int set, int epi, int nt, hipStream_t s);
+// K must be a multiple of 128.
+hipError_t launch_gemm_large_m(const GemmParams& p, int set, int epi, hipStream_t s);
 
 hipError_t launch_align(const int32_t* topk_ids, int T, int topk, int E, const RoutingLayout& L,
                         int32_t* routing, hipStream_t s);
