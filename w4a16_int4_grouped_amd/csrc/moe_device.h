@@ -37,14 +37,14 @@ __device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t m
   return r;
 }
 
-// Per-group constants of dq8: the scale s, s/16, -1032 s and -72 s (all
-// exact for |s| < 2^117, subnormal s included).
+// Per-group constants of dq8: the scale s, -1032 s and -72 s (all exact for
+// |s| < 2^117, subnormal s included).
 struct GroupScale {
-  float s, s16, c0, c1;
+  float s, c0, c1;
 };
 
 __device__ __forceinline__ GroupScale group_scale(float s) {
-  return GroupScale{s, s * 0.0625f, s * -1032.0f, s * -72.0f};
+  return GroupScale{s, s * -1032.0f, s * -72.0f};
 }
 
 // Dequantise one packed word: eight uint4 values q, low nibble first along
@@ -53,10 +53,11 @@ __device__ __forceinline__ GroupScale group_scale(float s) {
 // unfused BF16 rounding order).
 //
 // Nibbles 0 and 4 masked into the mantissas of an FP16 pair with exponent
-// bits 0x6400 read as 1024 + q; nibbles 1 and 5, masked in place one nibble
-// higher, read as 1024 + 16 q; nibbles 2, 6 and 3, 7 likewise after one
-// 8-bit shift. v_fma_mix_f32 widens one FP16 half and computes
-//   (1024 + q) s - 1032 s   or   (1024 + 16 q) (s/16) - 72 s,
+// bits 0x6400 (1024.0, unit step 1) read as 1024 + q; nibbles 1 and 5,
+// masked in place one nibble higher under exponent bits 0x5400 (64.0, step
+// 1/16), read as 64 + q; nibbles 2, 6 and 3, 7 likewise after one 8-bit
+// shift. v_fma_mix_f32 widens one FP16 half and computes
+//   (1024 + q) s - 1032 s   or   (64 + q) s - 72 s,
 // exactly (q - 8) s before its single rounding, and (q - 8) s has at most
 // 4 + 8 significant bits, so the FP32 result is exact; v_cvt_pk_bf16_f32
 // then rounds it once to BF16: bf16_rne((q - 8) s) for every nonzero
@@ -64,28 +65,30 @@ __device__ __forceinline__ GroupScale group_scale(float s) {
 // (x - x = +0); no MFMA result can tell +0 from -0 here, since the
 // accumulators start at +0 and +0 + -0 = +0. 17 VALU instructions per 8
 // weights. Result dword m holds k = 2m (low half) and k = 2m+1 (high half).
-__device__ __forceinline__ u32x4_t dq8(uint32_t w, const GroupScale& g, uint32_t magic) {
+__device__ __forceinline__ u32x4_t dq8(uint32_t w, const GroupScale& g, uint32_t magic_lo,
+                                      uint32_t magic_hi) {
   const uint32_t w8 = w >> 8;
-  const f16x2_t r0 = __builtin_bit_cast(f16x2_t, and_or(w, 0x000F000Fu, magic));    // q0, q4
-  const f16x2_t r1 = __builtin_bit_cast(f16x2_t, and_or(w, 0x00F000F0u, magic));    // q1, q5
-  const f16x2_t r2 = __builtin_bit_cast(f16x2_t, and_or(w8, 0x000F000Fu, magic));   // q2, q6
-  const f16x2_t r3 = __builtin_bit_cast(f16x2_t, and_or(w8, 0x00F000F0u, magic));   // q3, q7
+  const f16x2_t r0 = __builtin_bit_cast(f16x2_t, and_or(w, 0x000F000Fu, magic_lo));    // q0, q4
+  const f16x2_t r1 = __builtin_bit_cast(f16x2_t, and_or(w, 0x00F000F0u, magic_hi));    // q1, q5
+  const f16x2_t r2 = __builtin_bit_cast(f16x2_t, and_or(w8, 0x000F000Fu, magic_lo));   // q2, q6
+  const f16x2_t r3 = __builtin_bit_cast(f16x2_t, and_or(w8, 0x00F000F0u, magic_hi));   // q3, q7
   u32x4_t r;
-  r[0] = pack_bf16x2(__builtin_fmaf((float)r0[0], g.s, g.c0), __builtin_fmaf((float)r1[0], g.s16, g.c1));
-  r[1] = pack_bf16x2(__builtin_fmaf((float)r2[0], g.s, g.c0), __builtin_fmaf((float)r3[0], g.s16, g.c1));
-  r[2] = pack_bf16x2(__builtin_fmaf((float)r0[1], g.s, g.c0), __builtin_fmaf((float)r1[1], g.s16, g.c1));
-  r[3] = pack_bf16x2(__builtin_fmaf((float)r2[1], g.s, g.c0), __builtin_fmaf((float)r3[1], g.s16, g.c1));
+  r[0] = pack_bf16x2(__builtin_fmaf((float)r0[0], g.s, g.c0), __builtin_fmaf((float)r1[0], g.s, g.c1));
+  r[1] = pack_bf16x2(__builtin_fmaf((float)r2[0], g.s, g.c0), __builtin_fmaf((float)r3[0], g.s, g.c1));
+  r[2] = pack_bf16x2(__builtin_fmaf((float)r0[1], g.s, g.c0), __builtin_fmaf((float)r1[1], g.s, g.c1));
+  r[3] = pack_bf16x2(__builtin_fmaf((float)r2[1], g.s, g.c0), __builtin_fmaf((float)r3[1], g.s, g.c1));
   return r;
 }
 
-constexpr uint32_t kF16Magic = 0x64006400u;   // two FP16 1024.0
+constexpr uint32_t kF16MagicLo = 0x64006400u;   // two FP16 1024.0
+constexpr uint32_t kF16MagicHi = 0x54005400u;   // two FP16 64.0
 
 // dq8 with the sign of zero products set as in (q - 8) * s (sign of q - 8
 // times sign of s, +0 for q = 8 with s > 0): bit-identical to
 // bf16_rne((q - 8) * s) everywhere. Used where the dequantised weights
 // themselves are the result.
 __device__ __forceinline__ u32x4_t dq8_exact(uint32_t w, const GroupScale& g) {
-  u32x4_t r = dq8(w, g, kF16Magic);
+  u32x4_t r = dq8(w, g, kF16MagicLo, kF16MagicHi);
   const uint32_t s_neg = (__float_as_uint(g.s) >> 31) & 1u;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {

@@ -75,184 +75,262 @@ __device__ __forceinline__ void dma_tile(u32x4_t* lds_buf, const char* src0, con
   }
 }
 
-__device__ __forceinline__ void mma_chunk_l(const AFragL& f, const u32x4_t* lds_buf, const int (&rd)[4],
-                                            f32x4_t (&acc)[kMT][8], uint32_t magic) {
+// One K chunk: 4 MFMA steps g of 32 k over the first NTE token tiles. The
+// token fragments of a step stay in registers while the wave's 4 weight
+// tiles pass one at a time; each tile's MFMAs carry the dequantisation of
+// the next tile (17 VALU instructions) and, on the last tile of a step, the
+// LDS reads of the next step's token fragments, interleaved so the matrix
+// core and the vector ALU work side by side within the wave.
+template <int NTE>
+__device__ __forceinline__ void mma_chunk_l(const AFragL& f, const u32x4_t* lds_buf, int rd0,
+                                            f32x4_t (&acc)[kMT][NTE], uint32_t mlo, uint32_t mhi) {
+  constexpr int kValuPerMfma = NTE >= 8 ? 2 : (17 + NTE - 1) / NTE;
   GroupScale gs[kMT];
   {
     const float sc[4] = {bf16_lo(f.S[0]), bf16_hi(f.S[0]), bf16_lo(f.S[1]), bf16_hi(f.S[1])};
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) gs[mt] = group_scale(sc[mt]);
   }
+  u32x4_t b[NTE];
+#pragma unroll
+  for (int nt = 0; nt < NTE; ++nt) b[nt] = lds_buf[rd0 + nt * 256];
+  u32x4_t a = dq8(f.A[0][0], gs[0], mlo, mhi);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    u32x4_t a[kMT];
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) a[mt] = dq8(f.A[mt][g], gs[mt], magic);
+    for (int mt = 0; mt < kMT; ++mt) {
+      const bool last = (mt == kMT - 1);
+      const int ng = last ? g + 1 : g, nmt = last ? 0 : mt + 1;
+      u32x4_t an = a;
+      if (ng < 4) an = dq8(f.A[nmt][ng], gs[nmt], mlo, mhi);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const u32x4_t b = lds_buf[rd[g] + nt * 256];
+      for (int nt = 0; nt < NTE; ++nt) {
+        acc[mt][nt] = mfma16(a, b[nt], acc[mt][nt]);
+        // the step's last use of b[nt]: its register takes the next step's
+        if (last && g < 3) b[nt] = lds_buf[(rd0 ^ (g + 1)) + nt * 256];
+      }
+      // issue order within the region: each MFMA followed by its share of
+      // the vector work (and of the next step's LDS reads)
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) acc[mt][nt] = mfma16(a[mt], b, acc[mt][nt]);
+      for (int i = 0; i < NTE; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+        if (last && g < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);         // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      a = an;
+    }
+  }
+}
+
+// The K loop of one tile over its first NTE token tiles: chunk c+1's token
+// tile (only the waves whose rows are read load theirs) and weights are
+// fetched while chunk c is computed.
+template <int NTE>
+__device__ __forceinline__ void k_loop(u32x4_t (&lds)[2][kBufU4], const char* src0, const char* src1,
+                                       int wave, int lane, const u32x4_t* __restrict__ wq,
+                                       const u32x2_t* __restrict__ ws, int Kc, int rd0,
+                                       f32x4_t (&acc)[kMT][NTE]) {
+  const bool loader = 2 * wave < NTE;   // this wave's 32 rows are read
+  const uint32_t mlo = kF16MagicLo, mhi = kF16MagicHi;
+  AFragL fa, fb;
+  __syncthreads();   // the previous tile's readers are done with buffer 0
+  if (loader) dma_tile(lds[0], src0, src1, 0, wave);
+  load_a_l(fa, wq, ws, lane);
+  __syncthreads();
+
+  // step: compute chunk c from (CUR, buffer BUF); chunk c+1 is fetched into
+  // (NXT, the other buffer) first.
+#define MOE_LARGE_M_STEP(BUF, CUR, NXT, C)                                                    \
+  if ((C) < Kc) {                                                                             \
+    if ((C) + 1 < Kc) {                                                                       \
+      if (loader) dma_tile(lds[(BUF) ^ 1], src0, src1, (C) + 1, wave);                        \
+      load_a_l(NXT, wq + (size_t)((C) + 1) * (kMT * 64), ws + (size_t)((C) + 1) * 64, lane);  \
+    }                                                                                         \
+    mma_chunk_l<NTE>(CUR, lds[BUF], rd0, acc, mlo, mhi);                                      \
+    __syncthreads();                                                                          \
+  }
+  for (int kc = 0; kc < Kc; kc += 2) {
+    MOE_LARGE_M_STEP(0, fa, fb, kc)
+    MOE_LARGE_M_STEP(1, fb, fa, kc + 1)
+  }
+#undef MOE_LARGE_M_STEP
+}
+
+// Per-workgroup state of one row set.
+struct TileCtx {
+  const u32x4_t* wq;
+  const u32x2_t* ws;
+  int lane, wave, rg, e, slot0, count, rd0;
+  bool active;
+};
+
+// One token tile (rows tb .. tb + 128 of the set, `rows` of them worth
+// computing): source rows, the K loop over the first NTE token tiles, and
+// the epilogue. Each NTE is a complete body, so no accumulator is live
+// across the choice.
+template <int SET, int EPI, int NTE>
+__device__ __forceinline__ void run_tile(const GemmParams& p, const TileCtx& c,
+                                         u32x4_t (&lds)[2][kBufU4], int tb, int rows) {
+  constexpr bool kGather = (SET == SET_ROUTED && EPI == EPI_SWIGLU);
+  const int lane = c.lane, wave = c.wave;
+  // DMA source: this lane writes row 16*q + (lane >> 2) of a row block, in
+  // position (lane & 3), which holds piece (lane & 3) ^ swz(lane >> 2).
+  const int dma_piece = ((lane & 3) ^ swz(lane >> 2)) * 16;
+  const char* src[2];
+#pragma unroll
+  for (int ql = 0; ql < 2; ++ql) {
+    const int r = tb + 32 * wave + 16 * ql + (lane >> 2);   // tile row
+    int row;
+    if constexpr (SET == SET_ROUTED) {
+      if constexpr (kGather) {
+        const int f = p.sorted_ids[c.slot0 + r];
+        row = (f >= 0 && f < p.sentinel) ? f / p.topk : 0;   // pad slots read row 0
+      } else {
+        row = c.slot0 + r;
+      }
+    } else if constexpr (SET == SET_MASKED) {
+      row = c.slot0 + min(r, c.count - 1);   // pad rows repeat a valid row
+    } else {
+      row = c.slot0 + r;
+    }
+    src[ql] = reinterpret_cast<const char*>(p.src + (size_t)row * p.src_ld) + dma_piece;
+  }
+
+  f32x4_t acc[kMT][NTE];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTE; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  k_loop<NTE>(lds, src[0], src[1], wave, lane, c.wq, c.ws, p.Kc, c.rd0, acc);
+  if (!c.active) return;
+
+  // ---- epilogue
+  const int rg = c.rg;
+#pragma unroll
+  for (int nt = 0; nt < NTE; ++nt) {
+    const int r = tb + nt * 16 + (lane & 15);
+    if (r >= c.count || r - tb >= rows) continue;
+    const int slot = c.slot0 + r;
+    if constexpr (EPI == EPI_SWIGLU) {
+      if constexpr (SET == SET_ROUTED) {
+        const int f = p.sorted_ids[slot];
+        if (f < 0 || f >= p.sentinel) continue;   // pad slot: never read back
+      }
+      uint16_t* dst = p.a_out + (size_t)slot * p.a_ld + rg * 32 + (lane >> 4) * 4;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const f32x4_t g = acc[2 * pp][nt], u = acc[2 * pp + 1][nt];
+        u32x2_t v;
+        v[0] = pack_bf16x2(swiglu(g[0], u[0]), swiglu(g[1], u[1]));
+        v[1] = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
+        *reinterpret_cast<u32x2_t*>(dst + pp * 16) = v;
+      }
+    } else if constexpr (EPI == EPI_COMBINE) {
+      int f;
+      if constexpr (SET == SET_ROUTED) {
+        f = p.sorted_ids[slot];
+      } else {
+        f = (p.m_indices[slot] == c.e) ? p.row_src[slot] : -1;
+      }
+      if (f < 0 || f >= p.sentinel) continue;
+      const float w = p.topk_w[f];
+      float* dst = p.yrows + (size_t)f * p.yrows_ld;
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+        const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
+        if (n < p.N) *reinterpret_cast<f32x4_t*>(dst + n) = w * acc[mt][nt];
+      }
+    } else {
+      uint16_t* dst = p.out + (size_t)slot * p.out_ld;
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+        const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
+        if (n < p.N) {
+          u32x2_t v;
+          v[0] = pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]);
+          v[1] = pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]);
+          *reinterpret_cast<u32x2_t*>(dst + n) = v;
+        }
+      }
     }
   }
 }
 
 template <int SET, int EPI>
 __global__ __launch_bounds__(256, 2) void gemm_large_m(const GemmParams p) {
-  constexpr bool kGather = (SET == SET_ROUTED && EPI == EPI_SWIGLU);
   __shared__ u32x4_t lds[2][kBufU4];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  TileCtx c;
+  c.lane = threadIdx.x & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = c.lane;
   const int logical = xcd_remap(blockIdx.x, p.total_wg);
   const int set = logical / p.wg_per_set;
-  const int rg_raw = (logical - set * p.wg_per_set) * 4 + wave;
-  const bool active = rg_raw < p.RG;
-  const int rg = active ? rg_raw : p.RG - 1;
+  const int rg_raw = (logical - set * p.wg_per_set) * 4 + c.wave;
+  c.active = rg_raw < p.RG;
+  c.rg = c.active ? rg_raw : p.RG - 1;
 
-  // ---- the row set (uniform over the workgroup)
-  int e, slot0, count;
+  // ---- the row set (uniform over the workgroup). n_eff: one past the last
+  // valid row of the (single) tile of a routing or contiguous block; token
+  // tiles past it are neither loaded nor computed.
+  int n_eff = kBM;
   if constexpr (SET == SET_ROUTED) {
     const int32_t* hdr = p.routing_hdr;
     if (hdr[HDR_MAGIC] != kRoutingMagic || hdr[HDR_BLOCK] != p.block || hdr[HDR_E] != p.E ||
         hdr[HDR_T] * hdr[HDR_TOPK] != p.sentinel)
       return;
-    e = p.block_expert[set];
-    slot0 = set * kBM;
-    count = kBM;
+    c.e = p.block_expert[set];
+    c.slot0 = set * kBM;
+    c.count = kBM;
+    if (c.e < 0 || c.e >= p.E) return;
+    int last = 0;
+#pragma unroll
+    for (int r = lane; r < kBM; r += 64) {
+      const int f = p.sorted_ids[c.slot0 + r];
+      if (f >= 0 && f < p.sentinel) last = r + 1;
+    }
+    n_eff = __builtin_amdgcn_readfirstlane(wave_max(last));
   } else if constexpr (SET == SET_MASKED) {
-    e = set;
-    slot0 = e * p.max_m;
-    count = min(max(p.masked_m[e], 0), p.max_m);
-  } else {
-    slot0 = set * p.block_rows;
-    count = p.block_rows;
-    int m = -1;
-    for (int r = lane; r < p.block_rows; r += 64) {
-      const int v = p.m_indices[slot0 + r];
-      if (v >= 0 && v < p.E) m = max(m, v);
+    c.e = set;
+    c.slot0 = c.e * p.max_m;
+    c.count = min(max(p.masked_m[c.e], 0), p.max_m);
+  } else {   // contiguous blocks are one 128-row tile (block_rows == kBM)
+    c.slot0 = set * kBM;
+    c.count = kBM;
+    int m[2];
+    int mx = -1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      m[i] = p.m_indices[c.slot0 + lane + 64 * i];
+      if (m[i] >= 0 && m[i] < p.E) mx = max(mx, m[i]);
     }
-    e = wave_max(m);
+    c.e = wave_max(mx);
+    int last = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (m[i] == c.e) last = lane + 64 * i + 1;
+    n_eff = __builtin_amdgcn_readfirstlane(wave_max(last));
   }
-  if (count <= 0 || e < 0 || e >= p.E) return;
+  if (c.count <= 0 || c.e < 0 || c.e >= p.E || n_eff <= 0) return;
 
-  const size_t tile0 = ((size_t)e * p.RG + rg) * p.Kc;
-  const u32x4_t* __restrict__ wq = reinterpret_cast<const u32x4_t*>(p.wq) + tile0 * (kMT * 64);
-  const u32x2_t* __restrict__ ws = reinterpret_cast<const u32x2_t*>(p.wsc) + tile0 * 64;
-  const int Kc = p.Kc;
-  const uint32_t magic = kF16Magic;
+  const size_t tile0 = ((size_t)c.e * p.RG + c.rg) * p.Kc;
+  c.wq = reinterpret_cast<const u32x4_t*>(p.wq) + tile0 * (kMT * 64);
+  c.ws = reinterpret_cast<const u32x2_t*>(p.wsc) + tile0 * 64;
+  // B-fragment read offset (16-byte slots) of MFMA step 0 of a chunk: row
+  // (lane & 15) of row block 0, piece 4*(lane >> 4); step g reads slot
+  // rd0 ^ g (the swizzle sits in the low two bits), row block nt 256 on.
+  c.rd0 = (lane >> 4) * 64 + (lane & 15) * 4 + swz(lane & 15);
 
-  // B-fragment read offsets (16-byte slots) for the 4 MFMA steps of a chunk:
-  // row (lane & 15) of row block nt, piece 4*(lane >> 4) + g.
-  int rd[4];
-  {
-    const int rr = lane & 15;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) rd[g] = (lane >> 4) * 64 + rr * 4 + (g ^ swz(rr));
-  }
-  // DMA source: this lane writes row 16*q + (lane >> 2) of a row block, in
-  // position (lane & 3), which holds piece (lane & 3) ^ swz(lane >> 2).
-  const int dma_piece = ((lane & 3) ^ swz(lane >> 2)) * 16;
-
-  for (int tb = 0; tb < count; tb += kBM) {
-    const char* src[2];
-#pragma unroll
-    for (int ql = 0; ql < 2; ++ql) {
-      const int r = tb + 32 * wave + 16 * ql + (lane >> 2);   // tile row
-      int row;
-      if constexpr (SET == SET_ROUTED) {
-        if constexpr (kGather) {
-          const int f = p.sorted_ids[slot0 + r];
-          row = (f >= 0 && f < p.sentinel) ? f / p.topk : 0;   // pad slots read row 0
-        } else {
-          row = slot0 + r;
-        }
-      } else if constexpr (SET == SET_MASKED) {
-        row = slot0 + min(r, count - 1);   // pad rows repeat a valid row
-      } else {
-        row = slot0 + r;
-      }
-      src[ql] = reinterpret_cast<const char*>(p.src + (size_t)row * p.src_ld) + dma_piece;
-    }
-
-    f32x4_t acc[kMT][8];
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    AFragL fa, fb;
-    __syncthreads();   // the previous tile's readers are done with buffer 0
-    dma_tile(lds[0], src[0], src[1], 0, wave);
-    load_a_l(fa, wq, ws, lane);
-    __syncthreads();
-
-    // step: compute chunk c from (CUR, buffer BUF); chunk c+1 is fetched into
-    // (NXT, the other buffer) first.
-#define MOE_LARGE_M_STEP(BUF, CUR, NXT, C)                                                    \
-  if ((C) < Kc) {                                                                             \
-    if ((C) + 1 < Kc) {                                                                       \
-      dma_tile(lds[(BUF) ^ 1], src[0], src[1], (C) + 1, wave);                                \
-      load_a_l(NXT, wq + (size_t)((C) + 1) * (kMT * 64), ws + (size_t)((C) + 1) * 64, lane);  \
-    }                                                                                         \
-    mma_chunk_l(CUR, lds[BUF], rd, acc, magic);                                               \
-    __syncthreads();                                                                          \
-  }
-    for (int kc = 0; kc < Kc; kc += 2) {
-      MOE_LARGE_M_STEP(0, fa, fb, kc)
-      MOE_LARGE_M_STEP(1, fb, fa, kc + 1)
-    }
-#undef MOE_LARGE_M_STEP
-    if (!active) continue;
-
-    // ---- epilogue
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int r = tb + nt * 16 + (lane & 15);
-      if (r >= count) continue;
-      const int slot = slot0 + r;
-      if constexpr (EPI == EPI_SWIGLU) {
-        if constexpr (SET == SET_ROUTED) {
-          const int f = p.sorted_ids[slot];
-          if (f < 0 || f >= p.sentinel) continue;   // pad slot: never read back
-        }
-        uint16_t* dst = p.a_out + (size_t)slot * p.a_ld + rg * 32 + (lane >> 4) * 4;
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const f32x4_t g = acc[2 * pp][nt], u = acc[2 * pp + 1][nt];
-          u32x2_t v;
-          v[0] = pack_bf16x2(swiglu(g[0], u[0]), swiglu(g[1], u[1]));
-          v[1] = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
-          *reinterpret_cast<u32x2_t*>(dst + pp * 16) = v;
-        }
-      } else if constexpr (EPI == EPI_COMBINE) {
-        int f;
-        if constexpr (SET == SET_ROUTED) {
-          f = p.sorted_ids[slot];
-        } else {
-          f = (p.m_indices[slot] == e) ? p.row_src[slot] : -1;
-        }
-        if (f < 0 || f >= p.sentinel) continue;
-        const float w = p.topk_w[f];
-        float* dst = p.yrows + (size_t)f * p.yrows_ld;
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-          const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
-          if (n < p.N) *reinterpret_cast<f32x4_t*>(dst + n) = w * acc[mt][nt];
-        }
-      } else {
-        uint16_t* dst = p.out + (size_t)slot * p.out_ld;
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-          const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
-          if (n < p.N) {
-            u32x2_t v;
-            v[0] = pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]);
-            v[1] = pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]);
-            *reinterpret_cast<u32x2_t*>(dst + n) = v;
-          }
-        }
-      }
-    }
+  for (int tb = 0; tb < c.count; tb += kBM) {
+    const int rows = SET == SET_MASKED ? min(c.count - tb, kBM) : n_eff;   // uniform
+    if (rows <= 32)
+      run_tile<SET, EPI, 2>(p, c, lds, tb, rows);
+    else if (rows <= 64)
+      run_tile<SET, EPI, 4>(p, c, lds, tb, rows);
+    else if (rows <= 96)
+      run_tile<SET, EPI, 6>(p, c, lds, tb, rows);
+    else
+      run_tile<SET, EPI, 8>(p, c, lds, tb, rows);
   }
 }
 
@@ -261,6 +339,7 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m(const GemmParams p) {
 hipError_t launch_gemm_large_m(const GemmParams& p, int set, int epi, hipStream_t s) {
   if (p.total_wg <= 0) return hipSuccess;
   if (p.K % kKC) return hipErrorInvalidValue;   // whole chunks only
+  if (set == SET_BLOCKS && p.block_rows != kBM) return hipErrorInvalidValue;
   const dim3 grid(p.total_wg), block(256);
 #define MOE_GEMM_CASE(SET_, EPI_)                                                  \
   if (set == SET_ && epi == EPI_) {                                                \

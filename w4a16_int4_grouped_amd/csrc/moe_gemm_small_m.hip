@@ -90,7 +90,8 @@ __device__ __forceinline__ void store_b(TileLds<NT>& lds, int buf, const u32x4_t
 
 template <int NT>
 __device__ __forceinline__ void mma_chunk(const AFrag& f, const TileLds<NT>& lds, int buf,
-                                          f32x4_t (&acc)[kMT][NT], uint32_t magic) {
+                                          f32x4_t (&acc)[kMT][NT], uint32_t mlo,
+                                          uint32_t mhi) {
   const int lane = threadIdx.x & 63;
   const uint16_t* brow = &lds.b[buf][0][lane & 15][(lane >> 4) * 32];
   const float sc[4] = {bf16_lo(f.S[0]), bf16_hi(f.S[0]), bf16_lo(f.S[1]), bf16_hi(f.S[1])};
@@ -104,7 +105,7 @@ __device__ __forceinline__ void mma_chunk(const AFrag& f, const TileLds<NT>& lds
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         bf[nt] = *reinterpret_cast<const u32x4_t*>(brow + nt * (16 * kBRow) + g * 8);
-      const u32x4_t a = dq8(f.A[mt][g], gs, magic);
+      const u32x4_t a = dq8(f.A[mt][g], gs, mlo, mhi);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16(a, bf[nt], acc[mt][nt]);
     }
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
   const u32x4_t* __restrict__ wq_dummy = reinterpret_cast<const u32x4_t*>(p.wq);
   const u32x2_t* __restrict__ ws_dummy = reinterpret_cast<const u32x2_t*>(p.wsc);
   const int Kc = p.Kc;
-  const uint32_t magic = kF16Magic;
+  const uint32_t mlo = kF16MagicLo, mhi = kF16MagicHi;
   const int lr = threadIdx.x >> 4;             // token row this thread loads into LDS
   const int lpiece = (threadIdx.x & 15) * 8;   // its k offset within a chunk
   const int kmax = p.K - lpiece;               // chunk kc is readable if kc*128 < kmax
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
     load_a(NXT2, more ? wq + (size_t)(c + 2) * cstride * (kMT * 64) : wq_dummy,                  \
            more ? ws + (size_t)(c + 2) * cstride * 64 : ws_dummy, lane);                         \
     __builtin_amdgcn_sched_barrier(0);                                                           \
-    if (c < Kc) mma_chunk<NT>(CUR, lds, J, acc, magic);                                          \
+    if (c < Kc) mma_chunk<NT>(CUR, lds, J, acc, mlo, mhi);                                          \
     __builtin_amdgcn_sched_barrier(0);                                                           \
     store_b<NT>(lds, (J + 1) % 3, st);                                                           \
     __syncthreads();                                                                             \
