@@ -2,20 +2,25 @@
 
 One step = one pass of the whole layer over one batch: alignment of the
 top-k routing, W13 grouped GEMM with fused dequantisation and SwiGLU, W2
-grouped GEMM with the top-k-weighted scatter-add, and the BF16 convert
-(the indexed entry point with internal alignment). Inputs are seeded
-synthetic tensors already resident in HBM when timing starts.
+grouped GEMM storing each routed row's routing-weighted output, and the
+top-k combine into BF16 (for the indexed layout: the entry point with
+internal alignment). Inputs are seeded synthetic tensors already resident in
+HBM when timing starts.
 
 Default workload: Kimi-K2.x-shaped decode, indexed layout (384 experts,
-hidden 7168, intermediate 2048, 448 tokens, top-8).
+hidden 7168, intermediate 2048, 448 tokens, top-8). --workload picks any of
+the five (synth.WORKLOADS).
 
-Prints one JSON line (rank 0). Per-kernel durations come from HIP events the
-library records around each launch on the launch stream during the timed
-steps.
+Prints one JSON line. Per-kernel durations come from HIP events the library
+records around each launch on the launch stream during the timed steps; the
+roofline's traffic is the rocprofv3 counter measurement recorded under
+profiles/ for the same kernel and workload (null when none matches the
+current sources).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,6 +30,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer µs/call; decode weight GB/s & prefill TFLOP/s as % of roofline"
+# HBM traffic of the dominant kernel as measured with rocprofv3 TCC counters
+# (profiles/); reported only while the sources it was measured on are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+TRAFFIC_SOURCES = ["moe_gemm_small_m.hip", "moe_gemm_large_m.hip", "moe_device.h", "moe_layout.h",
+                   "moe_launch.h", "moe_api.cpp"]
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense BF16 MFMA
 
@@ -37,7 +47,7 @@ def parse():
     ap.add_argument("--workload", type=int, default=1,
                     help="index into synth.WORKLOADS (1: the Kimi decode layer, the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-experts", type=int, default=8, help="experts in the oracle's timed sample")
+    ap.add_argument("--cpu-experts", type=int, default=48, help="experts in the oracle's timed sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (steps times), the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -58,6 +68,29 @@ def copy_calibration(mib, steps):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     print(json.dumps({"copy_bytes": n, "ms_per_copy": ms, "GBps_read_plus_write": 2 * n / ms / 1e6}))
+
+
+def sources_sha256():
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "w4a16_int4_grouped_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """Bytes read + written per launch by `kernel` on `workload`, from the
+    counter record, or None when there is none or the sources changed."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            recs = json.load(f)
+    except (OSError, ValueError):
+        return None
+    sha = sources_sha256()
+    for r in recs:
+        if r["workload"] == workload and r["kernel"] == kernel and r["sources_sha256"] == sha:
+            return r["fetch_bytes"] + r["write_bytes"]
+    return None
 
 
 def log(*a):
@@ -207,6 +240,7 @@ def main():
         roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "avg_us": dom_us,
                 "flops_per_launch": work}
+    roof["traffic"] = measured_traffic(wl.name, dom)
     result = {
         "metric": METRIC,
         "value": ms * 1e3,
