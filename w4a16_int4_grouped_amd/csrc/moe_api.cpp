@@ -59,6 +59,7 @@ struct EnvOverrides {
   int schedule = 0;   // MOE_W4A16_SCHEDULE: 0 auto, 1 small-M, 2 large-M
   int nt = 0;         // MOE_W4A16_NT: token tiles per weight pass (1, 2, 4)
   int log = 0;        // MOE_W4A16_LOG: print each new schedule
+  int no_resident = 0;   // MOE_W4A16_NO_RESIDENT: keep the K-loop form of large-M for short K
   void read() {
     auto geti = [](const char* k) {
       const char* v = std::getenv(k);
@@ -67,6 +68,7 @@ struct EnvOverrides {
     schedule = geti("MOE_W4A16_SCHEDULE");
     nt = geti("MOE_W4A16_NT");
     log = geti("MOE_W4A16_LOG");
+    no_resident = geti("MOE_W4A16_NO_RESIDENT");
   }
 };
 
@@ -159,12 +161,30 @@ struct Schedule {
   int rows = 0;     // rows per expert the choice was made for
 };
 
+// Workgroups the K-resident large-M form aims for (about four per CU slot
+// of the 256 CUs at two workgroups each).
+constexpr int kResidentTargetWgs = 2048;
+
 // Launches one GEMM (mat 13 or 2) with the schedule's kernel, timed under a
-// fixed name.
-hipError_t run_gemm(int mat, const Schedule& sc, const GemmParams& p, int set, int epi, hipStream_t s) {
-  if (sc.kind == SCHED_LARGE_M)
+// fixed name. Large-M with K of one or two chunks on a routing or contiguous
+// row set takes the K-resident form: the token tile stays in LDS while a
+// workgroup walks several quads of output row groups.
+hipError_t run_gemm(int mat, const Schedule& sc, const GemmParams& p0, int set, int epi, hipStream_t s,
+                    bool allow_resident = true) {
+  if (sc.kind == SCHED_LARGE_M) {
+    GemmParams p = p0;
+    if (allow_resident && p.Kc <= 2 && set != SET_MASKED && p.nsets > 0) {
+      const int nquads = (p.RG + 3) / 4;
+      int wgs = (kResidentTargetWgs + p.nsets - 1) / p.nsets;
+      wgs = wgs < 1 ? 1 : (wgs > nquads ? nquads : wgs);
+      p.qpw = (nquads + wgs - 1) / wgs;
+      p.wg_per_set = (nquads + p.qpw - 1) / p.qpw;
+      p.total_wg = p.nsets * p.wg_per_set;
+    }
     return run(mat == 13 ? "gemm_w13_large_m" : "gemm_w2_large_m", s,
                [&] { return launch_gemm_large_m(p, set, epi, s); });
+  }
+  const GemmParams& p = p0;
   return run(mat == 13 ? "gemm_w13_small_m" : "gemm_w2_small_m", s,
              [&] { return launch_gemm_small_m(p, set, epi, sc.nt, s); });
 }
@@ -654,7 +674,7 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   p13.a_out = a_ws;
   p13.a_ld = I;
   if (e == hipSuccess)
-    e = run_gemm(13, sc, p13, set, EPI_SWIGLU, s);
+    e = run_gemm(13, sc, p13, set, EPI_SWIGLU, s, !h->env.no_resident);
 
   GemmParams p2 = p;
   fill_weights(p2, h, h->lay.w2);
@@ -665,7 +685,7 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   p2.topk_w = topk_w;
   p2.yrows_ld = H;
   if (e == hipSuccess)
-    e = run_gemm(2, sc, p2, set, EPI_COMBINE, s);
+    e = run_gemm(2, sc, p2, set, EPI_COMBINE, s, !h->env.no_resident);
   if (e == hipSuccess)
     e = run("combine_topk", s, [&] {
       return launch_combine_rows(yrows, rt + R.off_slot_of, rt, E, B, T, topk, H, out, s);
@@ -724,7 +744,7 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
   p13.a_out = a_ws;
   p13.a_ld = I;
   if (e == hipSuccess)
-    e = run_gemm(13, sc, p13, SET_BLOCKS, EPI_SWIGLU, s);
+    e = run_gemm(13, sc, p13, SET_BLOCKS, EPI_SWIGLU, s, !h->env.no_resident);
 
   GemmParams p2 = p;
   fill_weights(p2, h, h->lay.w2);
@@ -740,7 +760,7 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
         return launch_contiguous_valid(m_indices, row_src, M_pad, h->desc.num_experts, T * topk, valid, s);
       });
     if (e == hipSuccess)
-      e = run_gemm(2, sc, p2, SET_BLOCKS, EPI_COMBINE, s);
+      e = run_gemm(2, sc, p2, SET_BLOCKS, EPI_COMBINE, s, !h->env.no_resident);
     if (e == hipSuccess && T > 0)
       e = run("combine_topk", s, [&] {
         return launch_combine_rows(yrows, valid, nullptr, h->desc.num_experts, 0, T, topk, H, out, s);
@@ -749,7 +769,7 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
     p2.out = out;
     p2.out_ld = H;
     if (e == hipSuccess)
-      e = run_gemm(2, sc, p2, SET_BLOCKS, EPI_STORE, s);
+      e = run_gemm(2, sc, p2, SET_BLOCKS, EPI_STORE, s, !h->env.no_resident);
   }
   if (e != hipSuccess) return hip_fail(e, "contiguous launch");
   return ok();
@@ -794,7 +814,7 @@ moe_status_t moe_w4a16_masked(const moe_weights_t* hc, const uint16_t* a3, int32
   p13.src_ld = H;
   p13.a_out = a_ws;
   p13.a_ld = I;
-  hipError_t e = run_gemm(13, sc, p13, SET_MASKED, EPI_SWIGLU, s);
+  hipError_t e = run_gemm(13, sc, p13, SET_MASKED, EPI_SWIGLU, s, !h->env.no_resident);
 
   GemmParams p2 = p;
   fill_weights(p2, h, h->lay.w2);
@@ -804,7 +824,7 @@ moe_status_t moe_w4a16_masked(const moe_weights_t* hc, const uint16_t* a3, int32
   p2.out = out;
   p2.out_ld = H;
   if (e == hipSuccess)
-    e = run_gemm(2, sc, p2, SET_MASKED, EPI_STORE, s);
+    e = run_gemm(2, sc, p2, SET_MASKED, EPI_STORE, s, !h->env.no_resident);
   if (e != hipSuccess) return hip_fail(e, "masked launch");
   return ok();
 }

@@ -165,22 +165,19 @@ struct TileCtx {
   bool active;
 };
 
-// One token tile (rows tb .. tb + 128 of the set, `rows` of them worth
-// computing): source rows, the K loop over the first NTE token tiles, and
-// the epilogue. Each NTE is a complete body, so no accumulator is live
-// across the choice.
-template <int SET, int EPI, int NTE>
-__device__ __forceinline__ void run_tile(const GemmParams& p, const TileCtx& c,
-                                         u32x4_t (&lds)[2][kBufU4], int tb, int rows) {
+// This lane's two DMA source rows of token tile tb (row 32*wave + 16*ql +
+// lane/4 of the tile), each advanced to its swizzled 16-byte piece.
+template <int SET, int EPI>
+__device__ __forceinline__ void tile_sources(const GemmParams& p, const TileCtx& c, int tb,
+                                             const char* (&src)[2]) {
   constexpr bool kGather = (SET == SET_ROUTED && EPI == EPI_SWIGLU);
-  const int lane = c.lane, wave = c.wave;
+  const int lane = c.lane;
   // DMA source: this lane writes row 16*q + (lane >> 2) of a row block, in
   // position (lane & 3), which holds piece (lane & 3) ^ swz(lane >> 2).
   const int dma_piece = ((lane & 3) ^ swz(lane >> 2)) * 16;
-  const char* src[2];
 #pragma unroll
   for (int ql = 0; ql < 2; ++ql) {
-    const int r = tb + 32 * wave + 16 * ql + (lane >> 2);   // tile row
+    const int r = tb + 32 * c.wave + 16 * ql + (lane >> 2);   // tile row
     int row;
     if constexpr (SET == SET_ROUTED) {
       if constexpr (kGather) {
@@ -196,17 +193,13 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, const TileCtx& c,
     }
     src[ql] = reinterpret_cast<const char*>(p.src + (size_t)row * p.src_ld) + dma_piece;
   }
+}
 
-  f32x4_t acc[kMT][NTE];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NTE; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  k_loop<NTE>(lds, src[0], src[1], wave, lane, c.wq, c.ws, p.Kc, c.rd0, acc);
-  if (!c.active) return;
-
-  // ---- epilogue
-  const int rg = c.rg;
+// Writes the accumulators of row group rg for token rows tb .. tb + rows.
+template <int SET, int EPI, int NTE>
+__device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c, int tb, int rows,
+                                         int rg, const f32x4_t (&acc)[kMT][NTE]) {
+  const int lane = c.lane;
 #pragma unroll
   for (int nt = 0; nt < NTE; ++nt) {
     const int r = tb + nt * 16 + (lane & 15);
@@ -257,16 +250,169 @@ __device__ __forceinline__ void run_tile(const GemmParams& p, const TileCtx& c,
   }
 }
 
+// Row metadata of a resident tile, built once in LDS: for each tile row
+// the flat index f it feeds (-1: nothing to write) and its routing weight.
+struct RowMeta {
+  int32_t f[kBM];
+  float w[kBM];
+};
+
 template <int SET, int EPI>
+__device__ __forceinline__ void build_meta(const GemmParams& p, const TileCtx& c, RowMeta& m) {
+  for (int r = threadIdx.x; r < kBM; r += 256) {
+    const int slot = c.slot0 + r;
+    int f;
+    if constexpr (SET == SET_ROUTED) {
+      f = p.sorted_ids[slot];
+    } else if constexpr (EPI == EPI_COMBINE) {
+      f = (p.m_indices[slot] == c.e) ? p.row_src[slot] : -1;
+    } else {
+      f = 0;   // contiguous rows are written by slot
+    }
+    const bool ok = f >= 0 && (SET != SET_ROUTED && EPI != EPI_COMBINE ? true : f < p.sentinel);
+    m.f[r] = ok ? f : -1;
+    m.w[r] = (EPI == EPI_COMBINE && ok) ? p.topk_w[f] : 0.f;
+  }
+}
+
+// The epilogue of the resident form: row validity and weights from LDS.
+template <int SET, int EPI, int NTE>
+__device__ __forceinline__ void epilogue_meta(const GemmParams& p, const TileCtx& c, int rows, int rg,
+                                              const RowMeta& m, const f32x4_t (&acc)[kMT][NTE]) {
+  const int lane = c.lane;
+#pragma unroll
+  for (int nt = 0; nt < NTE; ++nt) {
+    const int r = nt * 16 + (lane & 15);
+    if (r >= rows) continue;
+    const int f = m.f[r];
+    if (f < 0) continue;
+    const int slot = c.slot0 + r;
+    if constexpr (EPI == EPI_SWIGLU) {
+      uint16_t* dst = p.a_out + (size_t)slot * p.a_ld + rg * 32 + (lane >> 4) * 4;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const f32x4_t g = acc[2 * pp][nt], u = acc[2 * pp + 1][nt];
+        u32x2_t v;
+        v[0] = pack_bf16x2(swiglu(g[0], u[0]), swiglu(g[1], u[1]));
+        v[1] = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
+        *reinterpret_cast<u32x2_t*>(dst + pp * 16) = v;
+      }
+    } else if constexpr (EPI == EPI_COMBINE) {
+      const float w = m.w[r];
+      float* dst = p.yrows + (size_t)f * p.yrows_ld;
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+        const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
+        if (n < p.N) *reinterpret_cast<f32x4_t*>(dst + n) = w * acc[mt][nt];
+      }
+    } else {
+      uint16_t* dst = p.out + (size_t)slot * p.out_ld;
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+        const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
+        if (n < p.N) {
+          u32x2_t v;
+          v[0] = pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]);
+          v[1] = pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]);
+          *reinterpret_cast<u32x2_t*>(dst + n) = v;
+        }
+      }
+    }
+  }
+}
+
+// One token tile (rows tb .. tb + 128 of the set, `rows` of them worth
+// computing): source rows, the K loop over the first NTE token tiles, and
+// the epilogue. Each NTE is a complete body, so no accumulator is live
+// across the choice.
+template <int SET, int EPI, int NTE>
+__device__ __forceinline__ void run_tile(const GemmParams& p, const TileCtx& c,
+                                         u32x4_t (&lds)[2][kBufU4], int tb, int rows) {
+  const char* src[2];
+  tile_sources<SET, EPI>(p, c, tb, src);
+  f32x4_t acc[kMT][NTE];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTE; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  k_loop<NTE>(lds, src[0], src[1], c.wave, c.lane, c.wq, c.ws, p.Kc, c.rd0, acc);
+  if (c.active) epilogue<SET, EPI, NTE>(p, c, 0 + tb, rows, c.rg, acc);
+}
+
+// K-resident form for K <= 256 (KCR = K / 128 chunks): the token tile is
+// loaded into LDS once (chunk c in buffer c) and the workgroup walks row
+// group quads q0 .. q1 of the output, each wave streaming its weights one
+// chunk ahead across quad boundaries. The tile is read-only after the first
+// barrier, so the loop has no barrier at all; a short-K GEMM with many
+// output rows (the down projection of a TP8 shard) no longer pays a
+// workgroup start and a tile load per 256 output rows.
+template <int SET, int EPI, int NTE, int KCR>
+__device__ __forceinline__ void run_tile_res(const GemmParams& p, const TileCtx& c,
+                                             u32x4_t (&lds)[2][kBufU4], RowMeta& meta, int rows,
+                                             int q0, int q1) {
+  const int lane = c.lane, wave = c.wave;
+  const uint32_t mlo = kF16MagicLo, mhi = kF16MagicHi;
+  const char* src[2];
+  tile_sources<SET, EPI>(p, c, 0, src);
+  if (2 * wave < NTE) {   // this wave's 32 rows are read
+#pragma unroll
+    for (int kc = 0; kc < KCR; ++kc) dma_tile(lds[kc], src[0], src[1], kc, wave);
+  }
+  // weights of (quad q, chunk kc) for this wave (row group clamped: waves
+  // past the last row group stream a valid one and skip the epilogue)
+  auto wq_of = [&](int q) {
+    const int rg = min(q * 4 + wave, p.RG - 1);
+    return ((size_t)c.e * p.RG + rg) * KCR;
+  };
+  const u32x4_t* __restrict__ wq0 = reinterpret_cast<const u32x4_t*>(p.wq);
+  const u32x2_t* __restrict__ ws0 = reinterpret_cast<const u32x2_t*>(p.wsc);
+  AFragL fa, fb;
+  {
+    const size_t t0 = wq_of(q0);
+    load_a_l(fa, wq0 + t0 * (kMT * 64), ws0 + t0 * 64, lane);
+  }
+  build_meta<SET, EPI>(p, c, meta);
+  __syncthreads();   // the token tile and the row metadata are in LDS
+  for (int q = q0; q < q1; ++q) {
+    // keep the epilogue's LDS reads inside the loop: hoisted, they would hold
+    // registers across the whole quad loop
+    asm volatile("" ::: "memory");
+    const int rg = q * 4 + wave;
+    const size_t t0 = wq_of(q);
+    const size_t tn = wq_of(q + 1 < q1 ? q + 1 : q);   // past the last quad: a valid repeat
+    f32x4_t acc[kMT][NTE];
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTE; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (KCR == 2) {
+      load_a_l(fb, wq0 + (t0 + 1) * (kMT * 64), ws0 + (t0 + 1) * 64, lane);
+      mma_chunk_l<NTE>(fa, lds[0], c.rd0, acc, mlo, mhi);
+      load_a_l(fa, wq0 + tn * (kMT * 64), ws0 + tn * 64, lane);
+      mma_chunk_l<NTE>(fb, lds[1], c.rd0, acc, mlo, mhi);
+    } else {
+      load_a_l(fb, wq0 + tn * (kMT * 64), ws0 + tn * 64, lane);
+      mma_chunk_l<NTE>(fa, lds[0], c.rd0, acc, mlo, mhi);
+      fa = fb;
+    }
+    if (rg < p.RG) epilogue_meta<SET, EPI, NTE>(p, c, rows, rg, meta, acc);
+  }
+}
+
+// KCR = 0: K-loop form, one quad of row groups per workgroup. KCR = 1 or 2
+// (K = 128 * KCR): K-resident form, p.qpw quads per workgroup.
+template <int SET, int EPI, int KCR>
 __global__ __launch_bounds__(256, 2) void gemm_large_m(const GemmParams p) {
   __shared__ u32x4_t lds[2][kBufU4];
+  __shared__ RowMeta meta;   // resident form only (1 KB; unused and dropped otherwise)
   TileCtx c;
   c.lane = threadIdx.x & 63;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = c.lane;
   const int logical = xcd_remap(blockIdx.x, p.total_wg);
   const int set = logical / p.wg_per_set;
-  const int rg_raw = (logical - set * p.wg_per_set) * 4 + c.wave;
+  const int wgi = logical - set * p.wg_per_set;
+  const int rg_raw = (KCR == 0 ? wgi : wgi * p.qpw) * 4 + c.wave;
   c.active = rg_raw < p.RG;
   c.rg = c.active ? rg_raw : p.RG - 1;
 
@@ -321,16 +467,30 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m(const GemmParams p) {
   // rd0 ^ g (the swizzle sits in the low two bits), row block nt 256 on.
   c.rd0 = (lane >> 4) * 64 + (lane & 15) * 4 + swz(lane & 15);
 
-  for (int tb = 0; tb < c.count; tb += kBM) {
-    const int rows = SET == SET_MASKED ? min(c.count - tb, kBM) : n_eff;   // uniform
+  if constexpr (KCR > 0) {   // one tile (routing or contiguous block), quads q0 .. q1
+    const int q0 = wgi * p.qpw, q1 = min(q0 + p.qpw, (p.RG + 3) / 4);
+    if (q0 >= q1) return;
+    const int rows = n_eff;
     if (rows <= 32)
-      run_tile<SET, EPI, 2>(p, c, lds, tb, rows);
+      run_tile_res<SET, EPI, 2, KCR>(p, c, lds, meta, rows, q0, q1);
     else if (rows <= 64)
-      run_tile<SET, EPI, 4>(p, c, lds, tb, rows);
+      run_tile_res<SET, EPI, 4, KCR>(p, c, lds, meta, rows, q0, q1);
     else if (rows <= 96)
-      run_tile<SET, EPI, 6>(p, c, lds, tb, rows);
+      run_tile_res<SET, EPI, 6, KCR>(p, c, lds, meta, rows, q0, q1);
     else
-      run_tile<SET, EPI, 8>(p, c, lds, tb, rows);
+      run_tile_res<SET, EPI, 8, KCR>(p, c, lds, meta, rows, q0, q1);
+  } else {
+    for (int tb = 0; tb < c.count; tb += kBM) {
+      const int rows = SET == SET_MASKED ? min(c.count - tb, kBM) : n_eff;   // uniform
+      if (rows <= 32)
+        run_tile<SET, EPI, 2>(p, c, lds, tb, rows);
+      else if (rows <= 64)
+        run_tile<SET, EPI, 4>(p, c, lds, tb, rows);
+      else if (rows <= 96)
+        run_tile<SET, EPI, 6>(p, c, lds, tb, rows);
+      else
+        run_tile<SET, EPI, 8>(p, c, lds, tb, rows);
+    }
   }
 }
 
@@ -341,9 +501,25 @@ hipError_t launch_gemm_large_m(const GemmParams& p, int set, int epi, hipStream_
   if (p.K % kKC) return hipErrorInvalidValue;   // whole chunks only
   if (set == SET_BLOCKS && p.block_rows != kBM) return hipErrorInvalidValue;
   const dim3 grid(p.total_wg), block(256);
+  if (p.qpw > 0) {   // K-resident form: K of 1 or 2 chunks, one tile per row set
+    if (p.Kc < 1 || p.Kc > 2 || set == SET_MASKED) return hipErrorInvalidValue;
+#define MOE_GEMM_RES(SET_, EPI_)                                                                   \
+  if (set == SET_ && epi == EPI_) {                                                                \
+    if (p.Kc == 1) hipLaunchKernelGGL((gemm_large_m<SET_, EPI_, 1>), grid, block, 0, s, p);       \
+    else hipLaunchKernelGGL((gemm_large_m<SET_, EPI_, 2>), grid, block, 0, s, p);                 \
+    return hipGetLastError();                                                                      \
+  }
+    MOE_GEMM_RES(SET_ROUTED, EPI_SWIGLU)
+    MOE_GEMM_RES(SET_ROUTED, EPI_COMBINE)
+    MOE_GEMM_RES(SET_BLOCKS, EPI_SWIGLU)
+    MOE_GEMM_RES(SET_BLOCKS, EPI_COMBINE)
+    MOE_GEMM_RES(SET_BLOCKS, EPI_STORE)
+#undef MOE_GEMM_RES
+    return hipErrorInvalidValue;
+  }
 #define MOE_GEMM_CASE(SET_, EPI_)                                                  \
   if (set == SET_ && epi == EPI_) {                                                \
-    hipLaunchKernelGGL((gemm_large_m<SET_, EPI_>), grid, block, 0, s, p);         \
+    hipLaunchKernelGGL((gemm_large_m<SET_, EPI_, 0>), grid, block, 0, s, p);      \
     return hipGetLastError();                                                      \
   }
   MOE_GEMM_CASE(SET_ROUTED, EPI_SWIGLU)

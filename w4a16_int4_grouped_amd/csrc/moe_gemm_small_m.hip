@@ -88,6 +88,12 @@ __device__ __forceinline__ void store_b(TileLds<NT>& lds, int buf, const u32x4_t
     *reinterpret_cast<u32x4_t*>(&lds.b[buf][nt][r][piece * 8]) = st[nt];
 }
 
+// One K chunk. NT = 1 (decode, 4 waves/SIMD at <= 128 registers): weight
+// tile outer, the single token fragment re-read from LDS per step. NT >= 2:
+// step outer; the step's NT token fragments stay in registers across the 4
+// weight tiles (one LDS read per token tile and step instead of four), and
+// each tile's MFMAs carry the next tile's dequantisation and, on the last
+// tile, the next step's LDS reads (issue order set by sched_group_barrier).
 template <int NT>
 __device__ __forceinline__ void mma_chunk(const AFrag& f, const TileLds<NT>& lds, int buf,
                                           f32x4_t (&acc)[kMT][NT], uint32_t mlo,
@@ -95,19 +101,49 @@ __device__ __forceinline__ void mma_chunk(const AFrag& f, const TileLds<NT>& lds
   const int lane = threadIdx.x & 63;
   const uint16_t* brow = &lds.b[buf][0][lane & 15][(lane >> 4) * 32];
   const float sc[4] = {bf16_lo(f.S[0]), bf16_hi(f.S[0]), bf16_lo(f.S[1]), bf16_hi(f.S[1])};
+  if constexpr (NT == 1) {
 #pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) {
-    const GroupScale gs = group_scale(sc[mt]);
+    for (int mt = 0; mt < kMT; ++mt) {
+      const GroupScale gs = group_scale(sc[mt]);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x4_t bf = *reinterpret_cast<const u32x4_t*>(brow + g * 8);
+        const u32x4_t a = dq8(f.A[mt][g], gs, mlo, mhi);
+        acc[mt][0] = mfma16(a, bf, acc[mt][0]);
+      }
+    }
+  } else {
+    constexpr int kValu = (17 + NT - 1) / NT;
+    GroupScale gs[kMT];
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) gs[mt] = group_scale(sc[mt]);
+    u32x4_t bf[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bf[nt] = *reinterpret_cast<const u32x4_t*>(brow + nt * (16 * kBRow));
+    u32x4_t a = dq8(f.A[0][0], gs[0], mlo, mhi);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      // token fragments are re-read from LDS per step to keep registers low
-      u32x4_t bf[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        bf[nt] = *reinterpret_cast<const u32x4_t*>(brow + nt * (16 * kBRow) + g * 8);
-      const u32x4_t a = dq8(f.A[mt][g], gs, mlo, mhi);
+      for (int mt = 0; mt < kMT; ++mt) {
+        const bool last = (mt == kMT - 1);
+        const int ng = last ? g + 1 : g, nmt = last ? 0 : mt + 1;
+        u32x4_t an = a;
+        if (ng < 4) an = dq8(f.A[nmt][ng], gs[nmt], mlo, mhi);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16(a, bf[nt], acc[mt][nt]);
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[mt][nt] = mfma16(a, bf[nt], acc[mt][nt]);
+          if (last && g < 3)
+            bf[nt] = *reinterpret_cast<const u32x4_t*>(brow + nt * (16 * kBRow) + (g + 1) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+          if (last && g < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+          __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);                // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        a = an;
+      }
     }
   }
 }

@@ -28,7 +28,8 @@ struct GemmParams {
   const void* wq;        // u32x4 [E][RG][Kc][4][64]
   const void* wsc;       // u16 [E][RG][Kc][64][4]
   int E, RG, Kc, K, N;   // N: true rows (output features)
-  int wg_per_set;        // workgroups per row set = ceil(RG / 4)
+  int wg_per_set;        // workgroups per row set: ceil(RG / 4), or ceil(ceil(RG / 4) / qpw)
+  int qpw;               // large-M K-resident form (K <= 256): row-group quads per workgroup; 0 off
   int nsets;             // row sets (experts or blocks)
   int total_wg;
   // row sets
@@ -58,7 +59,8 @@ struct GemmParams {
 };
 
 hipError_t launch_gemm_small_m(const GemmParams& p, int set, int epi, int nt, hipStream_t s);
-// K must be a multiple of 128.
+// K must be a multiple of 128; qpw > 0 (K-resident form) needs K <= 256 and
+// a routing or contiguous row set.
 hipError_t launch_gemm_large_m(const GemmParams& p, int set, int epi, hipStream_t s);
 
 hipError_t launch_align(const int32_t* topk_ids, int T, int topk, int E, const RoutingLayout& L,
