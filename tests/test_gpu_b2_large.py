@@ -146,3 +146,59 @@ def test_masked_large():
     ref = O.moe_masked(a3, mm, w)
     valid = np.concatenate([np.arange(e * max_m, e * max_m + mm[e]) for e in range(E)])
     check_tol(out[valid], ref[valid], "masked large-M")
+
+
+MULTI_BLOCK_CASES = [
+    # (E, H, I, T, topk, layout, with_row_src): K = 384 (3 chunks, an odd count)
+    # on both GEMMs, hundreds of rows per expert spread over up to 6 blocks
+    # with a Zipf skew, full and partial blocks side by side
+    (6, 384, 384, 800, 3, "indexed", True),
+    (5, 384, 384, 700, 2, "contiguous", True),
+    (5, 384, 384, 700, 2, "contiguous", False),
+]
+
+
+@pytest.mark.parametrize("E,H,I,T,topk,layout,with_src", MULTI_BLOCK_CASES)
+def test_multi_block_experts(E, H, I, T, topk, layout, with_src):
+    """Large-M K-loop GEMMs on experts spanning many 128-row blocks, every
+    epilogue (SwiGLU, weighted rows, row-wise BF16 store)."""
+    require_gpu()
+    import torch
+    log(f"case multi-block {layout} E={E} H={H} I={I} T={T} topk={topk} row_src={with_src}")
+    w = tiny_weights(E, H, I, seed=E * 11 + T)
+    x = synth.activations(91, T, H)
+    ids, tw = synth.zipf_routing(92, T, E, topk)
+    if layout == "indexed":
+        h = prepare(w, "indexed")
+        assert "schedule=large-M block=128" in describe(h, T, topk)
+        ids_d = i32_dev(ids)
+        routing = h.align(ids_d)
+        ws = torch.empty(h.workspace_bytes(T, topk, T), dtype=torch.uint8, device="cuda")
+        out = h.indexed(bf16_dev(x), ids_d, f32_dev(tw), routing=routing, ws=ws)
+        torch.cuda.synchronize()
+        ref, inter = O.moe_indexed(x, ids, tw, w, E=E, keep=True)
+        check_tol(O.bf16_to_f64(bits_host(out)), ref, "indexed multi-block")
+        lay = h.routing_layout(T, topk)
+        r = routing.cpu().numpy()
+        sid = r[lay.off_sorted:lay.off_sorted + lay.cap]
+        a_ws = ws[: lay.cap * I * 2].view(torch.int16).view(lay.cap, I).cpu().numpy().view(np.uint16)
+        slots = np.flatnonzero(sid < T * topk)
+        ref_a = np.stack([inter["a"][int(f)] for f in sid[slots]])
+        frac, mx, within = a_mismatch(a_ws[slots], ref_a, "indexed multi-block")
+        assert within and frac < 1e-3
+        return
+    a, m_idx, row_src = O.contiguous_layout(x, ids, E, 128)
+    a, m_idx, row_src = O.contiguous_layout(x, ids, E, 128, rows=a.shape[0] + 128)
+    a_nan = a.copy()
+    a_nan[m_idx < 0] = 0x7FC0
+    h = prepare(w, "contiguous")
+    describe(h, a.shape[0])
+    if with_src:
+        out = h.contiguous(bf16_dev(a_nan), i32_dev(m_idx), i32_dev(row_src), f32_dev(tw), T, topk)
+        ref = O.moe_contiguous(a, m_idx, w, row_src=row_src, topk_w=tw, T=T, topk=topk)
+        check_tol(O.bf16_to_f64(bits_host(out)), ref, "contiguous multi-block + combine")
+    else:
+        out = h.contiguous(bf16_dev(a_nan), i32_dev(m_idx))
+        ref = O.moe_contiguous(a, m_idx, w)
+        valid = m_idx >= 0
+        check_tol(O.bf16_to_f64(bits_host(out))[valid], ref[valid], "contiguous multi-block rows")

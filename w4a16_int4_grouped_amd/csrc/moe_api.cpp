@@ -170,10 +170,10 @@ constexpr int kResidentTargetWgs = 2048;
 // row set takes the K-resident form: the token tile stays in LDS while a
 // workgroup walks several quads of output row groups.
 hipError_t run_gemm(int mat, const Schedule& sc, const GemmParams& p0, int set, int epi, hipStream_t s,
-                    bool allow_resident = true) {
+                    const EnvOverrides& env) {
   if (sc.kind == SCHED_LARGE_M) {
     GemmParams p = p0;
-    if (allow_resident && p.Kc <= 2 && set != SET_MASKED && p.nsets > 0) {
+    if (!env.no_resident && p.Kc <= 2 && set != SET_MASKED && p.nsets > 0) {
       const int nquads = (p.RG + 3) / 4;
       int wgs = (kResidentTargetWgs + p.nsets - 1) / p.nsets;
       wgs = wgs < 1 ? 1 : (wgs > nquads ? nquads : wgs);
@@ -674,7 +674,7 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   p13.a_out = a_ws;
   p13.a_ld = I;
   if (e == hipSuccess)
-    e = run_gemm(13, sc, p13, set, EPI_SWIGLU, s, !h->env.no_resident);
+    e = run_gemm(13, sc, p13, set, EPI_SWIGLU, s, h->env);
 
   GemmParams p2 = p;
   fill_weights(p2, h, h->lay.w2);
@@ -685,7 +685,7 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   p2.topk_w = topk_w;
   p2.yrows_ld = H;
   if (e == hipSuccess)
-    e = run_gemm(2, sc, p2, set, EPI_COMBINE, s, !h->env.no_resident);
+    e = run_gemm(2, sc, p2, set, EPI_COMBINE, s, h->env);
   if (e == hipSuccess)
     e = run("combine_topk", s, [&] {
       return launch_combine_rows(yrows, rt + R.off_slot_of, rt, E, B, T, topk, H, out, s);
@@ -744,7 +744,7 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
   p13.a_out = a_ws;
   p13.a_ld = I;
   if (e == hipSuccess)
-    e = run_gemm(13, sc, p13, SET_BLOCKS, EPI_SWIGLU, s, !h->env.no_resident);
+    e = run_gemm(13, sc, p13, SET_BLOCKS, EPI_SWIGLU, s, h->env);
 
   GemmParams p2 = p;
   fill_weights(p2, h, h->lay.w2);
@@ -760,7 +760,7 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
         return launch_contiguous_valid(m_indices, row_src, M_pad, h->desc.num_experts, T * topk, valid, s);
       });
     if (e == hipSuccess)
-      e = run_gemm(2, sc, p2, SET_BLOCKS, EPI_COMBINE, s, !h->env.no_resident);
+      e = run_gemm(2, sc, p2, SET_BLOCKS, EPI_COMBINE, s, h->env);
     if (e == hipSuccess && T > 0)
       e = run("combine_topk", s, [&] {
         return launch_combine_rows(yrows, valid, nullptr, h->desc.num_experts, 0, T, topk, H, out, s);
@@ -769,7 +769,7 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
     p2.out = out;
     p2.out_ld = H;
     if (e == hipSuccess)
-      e = run_gemm(2, sc, p2, SET_BLOCKS, EPI_STORE, s, !h->env.no_resident);
+      e = run_gemm(2, sc, p2, SET_BLOCKS, EPI_STORE, s, h->env);
   }
   if (e != hipSuccess) return hip_fail(e, "contiguous launch");
   return ok();
@@ -814,7 +814,7 @@ moe_status_t moe_w4a16_masked(const moe_weights_t* hc, const uint16_t* a3, int32
   p13.src_ld = H;
   p13.a_out = a_ws;
   p13.a_ld = I;
-  hipError_t e = run_gemm(13, sc, p13, SET_MASKED, EPI_SWIGLU, s, !h->env.no_resident);
+  hipError_t e = run_gemm(13, sc, p13, SET_MASKED, EPI_SWIGLU, s, h->env);
 
   GemmParams p2 = p;
   fill_weights(p2, h, h->lay.w2);
@@ -824,7 +824,7 @@ moe_status_t moe_w4a16_masked(const moe_weights_t* hc, const uint16_t* a3, int32
   p2.out = out;
   p2.out_ld = H;
   if (e == hipSuccess)
-    e = run_gemm(2, sc, p2, SET_MASKED, EPI_STORE, s, !h->env.no_resident);
+    e = run_gemm(2, sc, p2, SET_MASKED, EPI_STORE, s, h->env);
   if (e != hipSuccess) return hip_fail(e, "masked launch");
   return ok();
 }

@@ -21,11 +21,8 @@
 //     chunk ahead into registers;
 //   * both are issued at the top of the chunk, so the barrier at its end
 //     (which waits for every outstanding load) finds them long arrived.
-// LDS layout of a buffer: blocks of 1 KB, block (q, s) holding rows
-// [16q, 16q+16) x 16-byte k pieces [4s, 4s+4); row rr of a block keeps its
-// 4 pieces in 64 B with piece p at position p ^ swz(rr). The swizzle makes
-// every MFMA B-fragment read (16 rows, one piece each) hit distinct banks,
-// whether the LDS serves 8 or 16 lanes of a 16-byte read per cycle.
+// The LDS layout of a buffer (swizzled 1 KB groups of 16 rows x 4 pieces)
+// is described in moe_tile.h.
 //
 // Row sets: a 128-slot block of the indexed routing (block 128; rows via
 // sorted_ids, pad slots hold the sentinel), a 128-row block of the
@@ -35,6 +32,7 @@
 
 #include "moe_device.h"
 #include "moe_launch.h"
+#include "moe_tile.h"
 
 namespace moe {
 
@@ -42,10 +40,6 @@ namespace {
 
 constexpr int kBM = 128;                       // token rows per tile
 constexpr int kBufU4 = kBM * kKC * 2 / 16;     // 16-byte slots per LDS buffer (2048)
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ int swz(int rr) { return ((rr >> 1) ^ (rr >> 2)) & 3; }
 
 struct AFragL {
   u32x4_t A[kMT];
@@ -57,22 +51,6 @@ __device__ __forceinline__ void load_a_l(AFragL& f, const u32x4_t* __restrict__ 
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) f.A[mt] = __builtin_nontemporal_load(wq + mt * 64 + lane);
   f.S = __builtin_nontemporal_load(ws + lane);
-}
-
-// This wave's share of the token tile of one chunk: row blocks 2w and 2w+1,
-// all four piece groups (8 x 1 KB). src0/src1: the lane's row pointers (with
-// its swizzled piece offset) at chunk 0.
-__device__ __forceinline__ void dma_tile(u32x4_t* lds_buf, const char* src0, const char* src1,
-                                         int kc, int wave) {
-#pragma unroll
-  for (int ql = 0; ql < 2; ++ql) {
-    const char* src = (ql ? src1 : src0) + (size_t)kc * (kKC * 2);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4_t* dst = lds_buf + ((2 * wave + ql) * 4 + s) * 64;
-      __builtin_amdgcn_global_load_lds(src + s * 64, (lds_void_t*)dst, 16, 0, 0);
-    }
-  }
 }
 
 // One K chunk: 4 MFMA steps g of 32 k over the first NTE token tiles. The
@@ -172,9 +150,7 @@ __device__ __forceinline__ void tile_sources(const GemmParams& p, const TileCtx&
                                              const char* (&src)[2]) {
   constexpr bool kGather = (SET == SET_ROUTED && EPI == EPI_SWIGLU);
   const int lane = c.lane;
-  // DMA source: this lane writes row 16*q + (lane >> 2) of a row block, in
-  // position (lane & 3), which holds piece (lane & 3) ^ swz(lane >> 2).
-  const int dma_piece = ((lane & 3) ^ swz(lane >> 2)) * 16;
+  const int piece = dma_piece(lane);
 #pragma unroll
   for (int ql = 0; ql < 2; ++ql) {
     const int r = tb + 32 * c.wave + 16 * ql + (lane >> 2);   // tile row
@@ -191,7 +167,7 @@ __device__ __forceinline__ void tile_sources(const GemmParams& p, const TileCtx&
     } else {
       row = c.slot0 + r;
     }
-    src[ql] = reinterpret_cast<const char*>(p.src + (size_t)row * p.src_ld) + dma_piece;
+    src[ql] = reinterpret_cast<const char*>(p.src + (size_t)row * p.src_ld) + piece;
   }
 }
 
@@ -462,10 +438,7 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m(const GemmParams p) {
   const size_t tile0 = ((size_t)c.e * p.RG + c.rg) * p.Kc;
   c.wq = reinterpret_cast<const u32x4_t*>(p.wq) + tile0 * (kMT * 64);
   c.ws = reinterpret_cast<const u32x2_t*>(p.wsc) + tile0 * 64;
-  // B-fragment read offset (16-byte slots) of MFMA step 0 of a chunk: row
-  // (lane & 15) of row block 0, piece 4*(lane >> 4); step g reads slot
-  // rd0 ^ g (the swizzle sits in the low two bits), row block nt 256 on.
-  c.rd0 = (lane >> 4) * 64 + (lane & 15) * 4 + swz(lane & 15);
+  c.rd0 = frag_rd0(lane);
 
   if constexpr (KCR > 0) {   // one tile (routing or contiguous block), quads q0 .. q1
     const int q0 = wgi * p.qpw, q1 = min(q0 + p.qpw, (p.RG + 3) / 4);
