@@ -126,6 +126,20 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return base + idx;
 }
 
+// xcd_remap over only the first `active` logical items of a grid of at
+// least that many workgroups: each XCD gets its share of the active items
+// as one contiguous range, and -1 for a workgroup beyond its XCD's share.
+// With a grid sized from an upper bound (routing capacity) and the active
+// count read on the device, the empty tail no longer lands on whole XCDs.
+__device__ __forceinline__ int xcd_remap_active(int b, int active) {
+  const int nx = 8;
+  const int xcd = b % nx, idx = b / nx;
+  const int per = active / nx, rem = active % nx;
+  if (idx >= per + (xcd < rem ? 1 : 0)) return -1;
+  const int base = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+  return base + idx;
+}
+
 __device__ __forceinline__ int wave_max(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));

@@ -385,7 +385,20 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m(const GemmParams p) {
   c.lane = threadIdx.x & 63;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = c.lane;
-  const int logical = xcd_remap(blockIdx.x, p.total_wg);
+  int logical;
+  if constexpr (SET == SET_ROUTED) {
+    // the grid covers the routing's capacity; only the blocks up to its
+    // padded total hold rows
+    const int32_t* hdr = p.routing_hdr;
+    if (hdr[HDR_MAGIC] != kRoutingMagic || hdr[HDR_BLOCK] != p.block || hdr[HDR_E] != p.E ||
+        hdr[HDR_T] * hdr[HDR_TOPK] != p.sentinel)
+      return;   // routing made for other shapes: compute nothing
+    const int nact = min(max(hdr[HDR_TOTAL], 0) / kBM, p.nsets);
+    logical = xcd_remap_active(blockIdx.x, nact * p.wg_per_set);
+    if (logical < 0) return;
+  } else {
+    logical = xcd_remap(blockIdx.x, p.total_wg);
+  }
   const int set = logical / p.wg_per_set;
   const int wgi = logical - set * p.wg_per_set;
   const int rg_raw = (KCR == 0 ? wgi : wgi * p.qpw) * 4 + c.wave;
@@ -397,10 +410,6 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m(const GemmParams p) {
   // tiles past it are neither loaded nor computed.
   int n_eff = kBM;
   if constexpr (SET == SET_ROUTED) {
-    const int32_t* hdr = p.routing_hdr;
-    if (hdr[HDR_MAGIC] != kRoutingMagic || hdr[HDR_BLOCK] != p.block || hdr[HDR_E] != p.E ||
-        hdr[HDR_T] * hdr[HDR_TOPK] != p.sentinel)
-      return;
     c.e = p.block_expert[set];
     c.slot0 = set * kBM;
     c.count = kBM;
@@ -473,6 +482,7 @@ hipError_t launch_gemm_large_m(const GemmParams& p, int set, int epi, hipStream_
   if (p.total_wg <= 0) return hipSuccess;
   if (p.K % kKC) return hipErrorInvalidValue;   // whole chunks only
   if (set == SET_BLOCKS && p.block_rows != kBM) return hipErrorInvalidValue;
+  if (set == SET_ROUTED && p.block != kBM) return hipErrorInvalidValue;
   const dim3 grid(p.total_wg), block(256);
   if (p.qpw > 0) {   // K-resident form: K of 1 or 2 chunks, one tile per row set
     if (p.Kc < 1 || p.Kc > 2 || set == SET_MASKED) return hipErrorInvalidValue;
