@@ -12,8 +12,9 @@
 // which is the stable order by flat index t*topk + j.
 //
 // Two paths:
-//   small (decode-sized routings): one workgroup of 16 waves counts, scans,
-//     fills the padding and places every row in a single launch;
+//   small (decode-sized routings, up to 4096 rows): one workgroup of 16
+//     waves counts, scans, fills the padding and places every row in a
+//     single launch;
 //   large: per-chunk counts, a one-workgroup scan over experts (which also
 //     turns the chunk counts into per-chunk prefixes), then one 4-wave
 //     workgroup per chunk places that chunk's rows.
@@ -28,23 +29,29 @@ namespace {
 
 constexpr int kCountThreads = 256;
 constexpr int kScanThreads = 1024;
-constexpr int kSmallMaxRows = 16384;   // small path limits
+constexpr int kSmallMaxRows = 16384;   // small path capacity (registers)
 constexpr int kSmallMaxExperts = 512;
+// Above this many rows the multi-workgroup path is faster (the one-workgroup
+// path places 1024 rows per round, about 1.7 us each).
+constexpr int kSmallPathRows = 4096;
 
 // Lanes of this wave routed to the same expert as this lane (e < 0: none).
-// Loops once per distinct expert in the wave.
-__device__ __forceinline__ uint64_t match_peers(int e) {
-  uint64_t todo = __ballot(e >= 0);
-  uint64_t peers = 0;
-  while (todo) {
-    const int j = __ffsll((unsigned long long)todo) - 1;
-    const int ej = __builtin_amdgcn_readlane(e, j);
-    const uint64_t m = __ballot(e == ej);
-    if (e == ej) peers = m;
-    todo &= ~m;
+// Matches the key e + 1 bit by bit: one ballot per key bit (nbits covers
+// 0 .. E), so the cost does not grow with the number of distinct experts in
+// the wave.
+__device__ __forceinline__ uint64_t match_peers(int e, int nbits) {
+  const int key = e + 1;
+  uint64_t m = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
   }
-  return peers;
+  return e >= 0 ? m : 0ull;
 }
+
+// Key bits for experts 0 .. E-1 plus "none".
+__device__ __forceinline__ int key_bits(int E) { return 32 - __builtin_clz((unsigned)E); }
 
 // Places flat rows [lo, hi) stably. next[e] (LDS) holds expert e's next free
 // slot and is advanced; cnt (LDS, NWAVES x E) must be zero on entry and is
@@ -63,7 +70,7 @@ __device__ void place_rows(const int32_t* __restrict__ ids, int lo, int hi, int 
       e = ids[f];
       if (e < 0 || e >= E) e = -1;
     }
-    const uint64_t peers = match_peers(e);
+    const uint64_t peers = match_peers(e, key_bits(E));
     const int rank = __popcll(peers & below);
     const bool leader = e >= 0 && rank == 0;
     if (leader) cnt[w * E + e] = __popcll(peers);
@@ -112,23 +119,22 @@ __device__ void scan_experts(int32_t* padded, int32_t* offsets, int E) {
   }
 }
 
-// Sentinels in pad slots, the block -> expert map and the header. (The
-// placement also writes slot_of[f], the slot of flat row f or -1 for a
-// dropped row, which the combine reads.)
-// start[0..E] holds the scanned offsets; counts the per-expert rows (NULL:
-// the caller has written the pad slots of each expert already).
-__device__ void fill_padding(int32_t* routing, const int32_t* start, const int32_t* counts, int E,
-                             int B, int T, int topk, int cap, int nblocks, int nchunks,
-                             int32_t* sorted_ids, int32_t* block_expert) {
+// Sentinels, the block -> expert map and the header. Every slot of
+// sorted_ids gets the sentinel (coalesced, all threads); placement, which
+// runs after a barrier or in a later kernel, overwrites the slots that hold
+// rows. start[0..E] holds the scanned offsets. (The placement also writes
+// slot_of[f], the slot of flat row f or -1 for a dropped row, which the
+// combine reads.)
+__device__ void fill_padding(int32_t* routing, const int32_t* start, int E, int B, int T, int topk,
+                             int cap, int nblocks, int nchunks, int32_t* sorted_ids,
+                             int32_t* block_expert) {
   const int sentinel = T * topk;
   const int total = start[E];
+  for (int q = threadIdx.x; q < cap; q += blockDim.x) sorted_ids[q] = sentinel;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const int s0 = start[e], s1 = start[e + 1];
-    if (counts)
-      for (int q = s0 + counts[e]; q < s1; ++q) sorted_ids[q] = sentinel;
     for (int b = s0 / B; b < s1 / B; ++b) block_expert[b] = e;
   }
-  for (int q = total + threadIdx.x; q < cap; q += blockDim.x) sorted_ids[q] = sentinel;
   for (int b = total / B + threadIdx.x; b < nblocks; b += blockDim.x) block_expert[b] = -1;
   if (threadIdx.x == 0) {
     routing[HDR_MAGIC] = kRoutingMagic;
@@ -183,15 +189,12 @@ __global__ __launch_bounds__(1024) void align_small(const int32_t* __restrict__ 
   __syncthreads();
   scan_experts(start, routing + off_offsets, E);
   __syncthreads();
+  fill_padding(routing, start, E, B, T, topk, cap, nblocks, 0, sorted_ids, routing + off_be);
   for (int e = threadIdx.x; e < E; e += 1024) {
     counts[e] = hist[e];
-    const int s0 = start[e], s1 = start[e + 1];
-    for (int q = s0 + hist[e]; q < s1; ++q) sorted_ids[q] = T * topk;
-    hist[e] = s0;   // next free slot
+    hist[e] = start[e];   // next free slot
   }
-  fill_padding(routing, start, nullptr, E, B, T, topk, cap, nblocks, 0, sorted_ids,
-               routing + off_be);
-  __syncthreads();
+  __syncthreads();   // sentinels stored before any row overwrites its slot
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(1024) void align_small(const int32_t* __restrict__ 
   for (int r = 0; r < kSmallRounds; ++r) {
     if (r >= rounds) break;   // uniform
     const int e = my_e[r];
-    const uint64_t peers = match_peers(e);
+    const uint64_t peers = match_peers(e, key_bits(E));
     const int rank = __popcll(peers & below);
     const bool leader = e >= 0 && rank == 0;
     if (leader) cnt[w * E + e] = __popcll(peers);
@@ -255,10 +258,15 @@ __global__ __launch_bounds__(kScanThreads) void align_scan(int32_t* __restrict__
   // per expert: exclusive prefix over chunks (in place) and the total
   for (int e = threadIdx.x; e < E; e += kScanThreads) {
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int h = chunk_hist[(size_t)c * E + e];
-      chunk_hist[(size_t)c * E + e] = run;
-      run += h;
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {   // 8 independent loads in flight
+      int h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = c0 + i < nchunks ? chunk_hist[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (c0 + i < nchunks) chunk_hist[(size_t)(c0 + i) * E + e] = run;
+        run += h[i];
+      }
     }
     counts[e] = run;
     padded[e] = (run + B - 1) / B * B;
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(kScanThreads) void align_scan(int32_t* __restrict__
   __syncthreads();
   scan_experts(padded, routing + off_offsets, E);
   __syncthreads();
-  fill_padding(routing, padded, counts, E, B, T, topk, cap, nblocks, nchunks, routing + off_sorted,
+  fill_padding(routing, padded, E, B, T, topk, cap, nblocks, nchunks, routing + off_sorted,
                routing + off_be);
 }
 
@@ -320,7 +328,7 @@ __global__ __launch_bounds__(256) void permute_rows(const uint16_t* __restrict__
 hipError_t launch_align(const int32_t* topk_ids, int T, int topk, int E, const RoutingLayout& L,
                         int32_t* routing, hipStream_t s) {
   const int n = T * topk;
-  if (n <= kSmallMaxRows && E <= kSmallMaxExperts) {
+  if (n <= kSmallPathRows && E <= kSmallMaxExperts) {
     const size_t lds = (size_t)(2 * (E + 1) + 16 * E) * sizeof(int32_t);
     hipLaunchKernelGGL(align_small, dim3(1), dim3(1024), lds, s, topk_ids, E, L.block, T, topk, L.cap,
                        L.nblocks, routing, L.off_counts, L.off_offsets, L.off_sorted,
