@@ -28,6 +28,8 @@ ROUTINGS = [
     ("cfg4", 384, 4096, 8, "softmax"),
     ("one-token", 5, 1, 3, "softmax"),
     ("ragged", 7, 1001, 3, "softmax"),
+    ("small-path-max", 64, 512, 8, "softmax"),   # 4096 rows: the one-workgroup path's limit
+    ("chunked-path-min", 64, 513, 8, "zipf"),    # 4104 rows: the smallest multi-workgroup case
 ]
 
 

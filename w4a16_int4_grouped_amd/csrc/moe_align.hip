@@ -29,11 +29,11 @@ namespace {
 
 constexpr int kCountThreads = 256;
 constexpr int kScanThreads = 1024;
-constexpr int kSmallMaxRows = 16384;   // small path capacity (registers)
+// One-workgroup path limits. Above 4096 rows the multi-workgroup path is
+// faster (the one-workgroup path places 1024 rows per round, about 1.7 us
+// each).
+constexpr int kSmallMaxRows = 4096;
 constexpr int kSmallMaxExperts = 512;
-// Above this many rows the multi-workgroup path is faster (the one-workgroup
-// path places 1024 rows per round, about 1.7 us each).
-constexpr int kSmallPathRows = 4096;
 
 // Lanes of this wave routed to the same expert as this lane (e < 0: none).
 // Matches the key e + 1 bit by bit: one ballot per key bit (nbits covers
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256) void permute_rows(const uint16_t* __restrict__
 hipError_t launch_align(const int32_t* topk_ids, int T, int topk, int E, const RoutingLayout& L,
                         int32_t* routing, hipStream_t s) {
   const int n = T * topk;
-  if (n <= kSmallPathRows && E <= kSmallMaxExperts) {
+  if (n <= kSmallMaxRows && E <= kSmallMaxExperts) {
     const size_t lds = (size_t)(2 * (E + 1) + 16 * E) * sizeof(int32_t);
     hipLaunchKernelGGL(align_small, dim3(1), dim3(1024), lds, s, topk_ids, E, L.block, T, topk, L.cap,
                        L.nblocks, routing, L.off_counts, L.off_offsets, L.off_sorted,
