@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=1,
                     help="index into synth.WORKLOADS (1: the Kimi decode layer, the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dispatch", type=int, default=0, choices=(0, 1, 2),
+                    help="indexed small-M token-tile dispatch: 0 semi-static grid (default), "
+                         "1 persistent static ranges, 2 persistent atomic job queue")
     ap.add_argument("--cpu-experts", type=int, default=48, help="experts in the oracle's timed sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (steps times), the "
@@ -163,13 +166,14 @@ def main():
         ids, tw = synth.routing(wl)
         x_d, ids_d, tw_d = to_dev(x, torch, np), to_dev(ids, torch, np), to_dev(tw, torch, np)
         out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(h.workspace_bytes(wl.T, wl.topk, wl.T), dtype=torch.uint8, device="cuda")
-        log(f"  schedule: {h.describe(wl.T, wl.topk)}")
+        ovr = {"dispatch": args.dispatch} if args.dispatch else None
+        ws = torch.empty(h.workspace_bytes(wl.T, wl.topk, wl.T, ovr=ovr), dtype=torch.uint8, device="cuda")
+        log(f"  schedule: {h.describe(wl.T, wl.topk, ovr=ovr)}")
         rows = wl.T * wl.topk
         touched = int(np.unique(ids[(ids >= 0) & (ids < wl.E)]).size)
 
         def step():
-            h.indexed(x_d, ids_d, tw_d, out=out, ws=ws, stream=stream)
+            h.indexed(x_d, ids_d, tw_d, out=out, ws=ws, stream=stream, ovr=ovr)
     elif wl.layout == "contiguous":
         # the contiguous input comes from the library's own align (block 128) + permute
         x = synth.activations(wl.iseed, wl.T, wl.H)
@@ -257,6 +261,7 @@ def main():
         "config": {"workload": wl.name, "layout": wl.layout, "experts": wl.E, "hidden": wl.H,
                    "intermediate": wl.I, "tokens": wl.T, "topk": wl.topk, "rows": rows,
                    "experts_touched": touched, "weights": "uint4 g32 bf16-scale",
+                   "dispatch": ["semi-static", "persistent-static", "persistent-queue"][args.dispatch],
                    "layer_packed_GBps": layer_packed / (ms * 1e-3) / 1e9,
                    "layer_packed_frac_hbm": layer_packed / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                    "layer_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,

@@ -88,11 +88,25 @@ typedef struct {
 /* Per-call schedule overrides, accepted by the indexed entry point only
  * (Chord page, "Grouped SM90 kernels": grouped dispatch owns its layout
  * search and rejects the indexed block_m / tuning overrides). A zero field
- * means "choose automatically". */
+ * means "choose automatically".
+ *
+ * dispatch (small-M schedule only; ignored under large-M) picks how the
+ * decode GEMMs' token tiles are scheduled, for the comparison the Chord page
+ * measured in "H200 and Blackwell indexed decode" (semi-static against fully
+ * dynamic):
+ *   0  semi-static (default): a grid fixed from host-known sizes, one
+ *      workgroup per (expert, 256 weight rows), row counts read on the device;
+ *   1  persistent, static: one workgroup per resident slot, each taking an
+ *      equal contiguous range of (routing block, 256 weight rows) jobs;
+ *   2  persistent, fully dynamic: the same workgroups taking jobs one at a
+ *      time from an atomic counter in the workspace (cleared by the call with
+ *      a fill kernel on its stream).
+ * With 1 or 2 the routing block is one weight pass, 16 x the token tiles
+ * (16, 32 or 64 rows), unless block_m sets it. */
 typedef struct {
   int32_t block_m;  /* alignment block (rows): 16, 32, 64 or 128 */
   int32_t schedule; /* 0 auto, 1 small-M (decode), 2 large-M (prefill) */
-  int32_t reserved0;
+  int32_t dispatch; /* small-M token-tile dispatch: 0, 1 or 2 (above) */
   int32_t reserved1;
 } moe_tuning_t;
 

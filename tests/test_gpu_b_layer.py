@@ -192,3 +192,58 @@ def test_layouts_agree_on_identical_routing():
     check_tol(out_i, ref, "indexed")
     check_tol(out_c, ref, "contiguous")
     check_tol(out_c, out_i, "contiguous vs indexed")
+
+
+DISPATCH_CASES = [
+    # (E, H, I, T, topk, grid cap or 0): the persistent small-M forms on
+    # routing blocks of one weight pass; capped grids make every workgroup
+    # walk many jobs across blocks. K chunks 1 (H 128, I 64 with a K tail),
+    # 2 (256) and 3 (384); one, two and four token tiles per pass.
+    (16, 128, 64, 40, 4, 0),
+    (16, 128, 64, 40, 4, 1),
+    (16, 256, 256, 100, 4, 3),
+    (8, 384, 384, 60, 4, 5),
+    (12, 256, 128, 120, 6, 2),
+    (384, 128, 64, 448, 8, 0),
+]
+
+
+@pytest.mark.parametrize("dispatch", [1, 2])
+@pytest.mark.parametrize("E,H,I,T,topk,wgs", DISPATCH_CASES)
+def test_indexed_small_dispatch(E, H, I, T, topk, wgs, dispatch, monkeypatch):
+    """Persistent static and job-queue dispatch against the oracle: outputs
+    and the intermediate a, with the weight and token streams running on
+    across job boundaries."""
+    require_gpu()
+    import torch
+    log(f"case dispatch={dispatch} E={E} H={H} I={I} T={T} topk={topk} wgs={wgs}")
+    if wgs:
+        monkeypatch.setenv("MOE_W4A16_JOB_WGS", str(wgs))
+    ovr = {"dispatch": dispatch}
+    w = tiny_weights(E, H, I, seed=E * 3 + I)
+    x = synth.activations(41, T, H)
+    ids, tw = synth.zipf_routing(42, T, E, topk)
+    ids = ids.copy()
+    ids[::7, 0] = -1
+    h = prepare(w, "indexed")
+    d = h.describe(T, topk, ovr=ovr)
+    log(f"  {d}")
+    assert "small-M" in d and "dispatch=persistent" in d
+    ids_d = i32_dev(ids)
+    routing = h.align(ids_d, ovr=ovr)
+    ws = torch.empty(h.workspace_bytes(T, topk, T, ovr=ovr), dtype=torch.uint8, device="cuda")
+    out = h.indexed(bf16_dev(x), ids_d, f32_dev(tw), routing=routing, ws=ws, ovr=ovr)
+    torch.cuda.synchronize()
+    ref, inter = O.moe_indexed(x, ids, tw, w, E=E, keep=True)
+    check_tol(O.bf16_to_f64(bits_host(out)), ref, f"indexed dispatch {dispatch}")
+    lay = h.routing_layout(T, topk, ovr)
+    r = routing.cpu().numpy()
+    sid = r[lay.off_sorted:lay.off_sorted + lay.cap]
+    a_ws = ws[: lay.cap * I * 2].view(torch.int16).view(lay.cap, I).cpu().numpy().view(np.uint16)
+    slots = np.flatnonzero(sid < T * topk)
+    ref_a = np.stack([inter["a"][int(f)] for f in sid[slots]])
+    frac, mx, within = a_mismatch(a_ws[slots], ref_a, f"indexed dispatch {dispatch}")
+    assert within and frac < 1e-3
+    # the same call again: the queue is cleared by each call
+    out2 = h.indexed(bf16_dev(x), ids_d, f32_dev(tw), routing=routing, ws=ws, ovr=ovr)
+    assert np.array_equal(bits_host(out2), bits_host(out))

@@ -58,7 +58,7 @@ def make_desc(E, H, I, mode="indexed", bits=4, group_size=32, zero_point=8,
 
 class Tuning(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int32), ("schedule", ctypes.c_int32),
-                ("reserved0", ctypes.c_int32), ("reserved1", ctypes.c_int32)]
+                ("dispatch", ctypes.c_int32), ("reserved1", ctypes.c_int32)]
 
 
 class RoutingLayout(ctypes.Structure):
@@ -151,7 +151,8 @@ def _tuning(ovr):
         return None
     if isinstance(ovr, Tuning):
         return ctypes.byref(ovr)
-    return ctypes.byref(Tuning(int(ovr.get("block_m", 0)), int(ovr.get("schedule", 0)), 0, 0))
+    return ctypes.byref(Tuning(int(ovr.get("block_m", 0)), int(ovr.get("schedule", 0)),
+                               int(ovr.get("dispatch", 0)), 0))
 
 
 def _empty(nbytes, device):

@@ -60,6 +60,7 @@ struct EnvOverrides {
   int nt = 0;         // MOE_W4A16_NT: token tiles per weight pass (1, 2, 4)
   int log = 0;        // MOE_W4A16_LOG: print each new schedule
   int no_resident = 0;   // MOE_W4A16_NO_RESIDENT: keep the K-loop form of large-M for short K
+  int job_wgs = 0;       // MOE_W4A16_JOB_WGS: cap on the persistent small-M grid (tests: long job walks)
   void read() {
     auto geti = [](const char* k) {
       const char* v = std::getenv(k);
@@ -69,6 +70,7 @@ struct EnvOverrides {
     nt = geti("MOE_W4A16_NT");
     log = geti("MOE_W4A16_LOG");
     no_resident = geti("MOE_W4A16_NO_RESIDENT");
+    job_wgs = geti("MOE_W4A16_JOB_WGS");
   }
 };
 
@@ -158,12 +160,27 @@ struct Schedule {
   int kind = SCHED_SMALL_M;
   int block = 16;   // routing alignment block (indexed)
   int nt = 1;       // 16-row token tiles per weight pass (small-M)
+  int dispatch = 0; // small-M: 0 semi-static grid, 1 persistent static ranges, 2 persistent job queue
   int rows = 0;     // rows per expert the choice was made for
 };
 
 // Workgroups the K-resident large-M form aims for (about four per CU slot
 // of the 256 CUs at two workgroups each).
 constexpr int kResidentTargetWgs = 2048;
+
+// Grid of the persistent small-M forms: one workgroup per resident slot (4,
+// 3 or 2 per CU by token tiles), and enough that no static job range spans
+// more than 62 routing blocks (the kernel keeps one entry per block of its
+// range in a 64-lane register).
+int job_grid(int nsets, int passes, int quads, int nt, const EnvOverrides& env) {
+  const int slots = 256 * (nt == 1 ? 4 : (nt == 2 ? 3 : 2));
+  const int64_t jobs = (int64_t)nsets * passes * quads;
+  int64_t g = jobs < slots ? jobs : slots;
+  if (env.job_wgs > 0 && g > env.job_wgs) g = env.job_wgs;
+  const int64_t gmin = (nsets + 59) / 60;
+  if (g < gmin) g = gmin;
+  return (int)g;
+}
 
 // Launches one GEMM (mat 13 or 2) with the schedule's kernel, timed under a
 // fixed name. Large-M with K of one or two chunks on a routing or contiguous
@@ -184,7 +201,8 @@ hipError_t run_gemm(int mat, const Schedule& sc, const GemmParams& p0, int set, 
     return run(mat == 13 ? "gemm_w13_large_m" : "gemm_w2_large_m", s,
                [&] { return launch_gemm_large_m(p, set, epi, s); });
   }
-  const GemmParams& p = p0;
+  GemmParams p = p0;
+  if (p.dispatch) p.total_wg = job_grid(p.nsets, p.passes, p.wg_per_set, sc.nt, env);
   return run(mat == 13 ? "gemm_w13_small_m" : "gemm_w2_small_m", s,
              [&] { return launch_gemm_small_m(p, set, epi, sc.nt, s); });
 }
@@ -217,6 +235,7 @@ uint64_t key_of(int mode, int a, int b, const moe_tuning_t* o) {
   if (o) {
     k = k * 1000003u + (uint32_t)o->block_m;
     k = k * 1000003u + (uint32_t)o->schedule;
+    k = k * 1000003u + (uint32_t)o->dispatch;
   }
   return k;
 }
@@ -256,7 +275,9 @@ Schedule schedule_indexed(moe_weights* h, int T, int topk, const moe_tuning_t* o
   if (!large_m_fits(h)) s.kind = SCHED_SMALL_M;
   s.nt = nt_for_rows((int)rows);
   if (h->env.nt) s.nt = h->env.nt;
-  s.block = s.kind == SCHED_LARGE_M ? 128 : 16;
+  if (ovr && s.kind == SCHED_SMALL_M) s.dispatch = ovr->dispatch;
+  // the persistent forms take one routing block per weight pass of 16*nt rows
+  s.block = s.kind == SCHED_LARGE_M ? 128 : (s.dispatch ? 16 * s.nt : 16);
   if (ovr && ovr->block_m) s.block = ovr->block_m;
   if (h->env.log)
     std::fprintf(stderr, "[moe_w4a16] indexed T=%d topk=%d rows/expert=%ld -> %s nt=%d block=%d\n",
@@ -348,7 +369,7 @@ moe_status_t check_topk(const moe_weights_t* h, int T, int topk) {
 // the second GEMM (one per flat routed row, summed by the combine), the
 // contiguous layout's row-validity map, and the indexed layout's own routing.
 struct WsLayout {
-  size_t off_a = 0, off_y = 0, off_valid = 0, off_routing = 0, total = 0;
+  size_t off_a = 0, off_y = 0, off_queue = 0, off_valid = 0, off_routing = 0, total = 0;
 };
 
 WsLayout ws_indexed(const moe_weights_t* h, int T, int topk, int block) {
@@ -360,6 +381,8 @@ WsLayout ws_indexed(const moe_weights_t* h, int T, int topk, int block) {
   o = round_up(o + (size_t)R.cap * h->desc.inter * 2, kAlign);
   w.off_y = o;
   o = round_up(o + (size_t)T * topk * h->desc.hidden * 4, kAlign);
+  w.off_queue = o;   // job counters of the persistent small-M dispatch (W13, W2)
+  o += kAlign;
   w.off_valid = w.off_routing = o;
   o = round_up(o + (size_t)R.total_ints * 4, kAlign);
   w.total = o;
@@ -505,6 +528,10 @@ int32_t moe_routing_block(const moe_weights_t* h, int32_t T, int32_t topk, const
   if (ovr && ovr->block_m && ovr->block_m != 16 && ovr->block_m != 32 && ovr->block_m != 64 &&
       ovr->block_m != 128) {
     fail(MOE_ERR_INVALID_ARG, "block_m %d not in {16, 32, 64, 128}", ovr->block_m);
+    return 0;
+  }
+  if (ovr && (ovr->dispatch < 0 || ovr->dispatch > 2)) {
+    fail(MOE_ERR_INVALID_ARG, "dispatch %d not in 0..2", ovr->dispatch);
     return 0;
   }
   if (large_m_rejected(h, ovr)) {
@@ -660,14 +687,24 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   p.topk = topk;
   p.block = B;
   p.block_expert = rt + R.off_block_expert;
-  // small-M: one row set per expert; large-M: one per 128-slot routing block
+  // semi-static small-M: one row set per expert; large-M and the persistent
+  // small-M forms: one per routing block
   const bool large = sc.kind == SCHED_LARGE_M;
-  p.nsets = large ? R.nblocks : E;
-  const int set = large ? SET_ROUTED : SET_INDEXED;
+  const bool blocks = large || sc.dispatch;
+  p.nsets = blocks ? R.nblocks : E;
+  const int set = blocks ? SET_ROUTED : SET_INDEXED;
+  if (!large && sc.dispatch) {
+    p.dispatch = sc.dispatch;
+    p.passes = (B + 16 * sc.nt - 1) / (16 * sc.nt);
+  }
+  int32_t* queue = (int32_t*)(wsb + W.off_queue);
+  if (e == hipSuccess && p.dispatch == 2)
+    e = run("zero_queue", s, [&] { return launch_zero_i32(queue, 2, s); });
 
   GemmParams p13 = p;
   fill_weights(p13, h, h->lay.w13);
   p13.total_wg = p13.nsets * p13.wg_per_set;
+  p13.queue = queue;
   p13.src = x;
   p13.src_ld = H;
   p13.gather = 1;
@@ -679,6 +716,7 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   GemmParams p2 = p;
   fill_weights(p2, h, h->lay.w2);
   p2.total_wg = p2.nsets * p2.wg_per_set;
+  p2.queue = queue + 1;
   p2.src = a_ws;
   p2.src_ld = I;
   p2.yrows = yrows;
@@ -858,11 +896,17 @@ int moe_describe(const moe_weights_t* hc, int32_t mode, int32_t rows, int32_t to
     const Schedule s = schedule_indexed(h, rows, topk, ovr);
     RoutingLayout R;
     R.init(E, rows, topk, s.block);
-    const int sets = s.kind == SCHED_LARGE_M ? R.nblocks : E;
+    const bool persistent = s.kind == SCHED_SMALL_M && s.dispatch;
+    const int sets = s.kind == SCHED_LARGE_M || persistent ? R.nblocks : E;
+    const int P = (s.block + 16 * s.nt - 1) / (16 * s.nt);
+    const int g13 = persistent ? job_grid(sets, P, wg13, s.nt, h->env) : sets * wg13;
+    const int g2 = persistent ? job_grid(sets, P, wg2, s.nt, h->env) : sets * wg2;
+    static const char* kDispatch[] = {"semi-static", "persistent-static", "persistent-queue"};
     len = std::snprintf(buf, n,
                         "layout=indexed T=%d topk=%d rows_per_expert=%d schedule=%s block=%d nt=%d "
-                        "grid_w13=%d grid_w2=%d",
-                        rows, topk, s.rows, kind_name(s.kind), s.block, s.nt, sets * wg13, sets * wg2);
+                        "grid_w13=%d grid_w2=%d dispatch=%s",
+                        rows, topk, s.rows, kind_name(s.kind), s.block, s.nt, g13, g2,
+                        s.kind == SCHED_SMALL_M ? kDispatch[s.dispatch] : "routing-blocks");
   } else if (mode == MOE_MODE_MASKED) {
     if (expected_m <= 0 || rows < 0) return -1;
     const Schedule s = schedule_masked(h, rows, expected_m);

@@ -302,9 +302,393 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
   }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent forms (routing blocks of one weight pass), for the dispatch
+// ablation of the Chord page ("H200 and Blackwell indexed decode"), which
+// measured its semi-static token-tile schedule (the grid above) against a
+// fully dynamic one.
+//
+// A job is one weight pass: (routing block, token pass, quad of row groups),
+// numbered block-major. One workgroup per resident slot walks a sequence of
+// jobs as one stream of K chunks: weights two chunks ahead and the token
+// tile one chunk ahead keep flowing across job boundaries. DYN = false: each
+// workgroup takes an equal contiguous range of the jobs (a static split,
+// ranges on one XCD each). DYN = true: workgroups take jobs one at a time
+// from an atomic counter (a fully dynamic work queue), two jobs ahead of the
+// one being computed.
+// ---------------------------------------------------------------------------
+
+// Jobs of a set: ceil(rows / (16*NT)) token passes x quads.
+struct JobSpace {
+  int P, Q;        // passes per set, quads per set
+  int s0;          // first set of this workgroup's range
+  int info;        // lane i: ROUTED: expert of set s0+i (-1 none); MASKED: rows of expert s0+i
+  int64_t j1;      // end of this workgroup's range
+};
+
+// One job's uniform data (SGPRs) and, for the current and next job, the
+// lane's token row pointers.
+struct Job {
+  int64_t j;       // job index; j >= j1: none
+  int e, slot0, count, tb, rg;
+  bool active;
+  const u32x4_t* wq;   // chunk 0 of this wave's row group
+  const u32x2_t* ws;
+};
+
+template <int SET>
+__device__ __forceinline__ bool job_valid(const JobSpace& js, int64_t j, int rows_per_pass) {
+  const int s = (int)(j / ((int64_t)js.P * js.Q));
+  const int v = __builtin_amdgcn_readlane(js.info, s - js.s0);
+  if constexpr (SET == SET_ROUTED) {
+    return v >= 0;
+  } else {
+    const int pass = (int)((j - (int64_t)s * js.P * js.Q) / js.Q);
+    return pass * rows_per_pass < v;
+  }
+}
+
+template <int SET>
+__device__ __forceinline__ int64_t next_job(const JobSpace& js, int64_t j, int rows_per_pass) {
+  do {
+    ++j;
+  } while (j < js.j1 && !job_valid<SET>(js, j, rows_per_pass));
+  return j;
+}
+
+// A job from its index and its set's info value (the expert of a routing
+// block; the rows of a masked expert).
+template <int SET>
+__device__ __forceinline__ Job make_job_e(const GemmParams& p, const JobSpace& js, int64_t j, int v,
+                                          int wave, int rows_per_pass) {
+  Job b;
+  b.j = j;
+  if (j >= js.j1) {   // none: valid dummy addresses
+    b.e = 0; b.slot0 = 0; b.count = 1; b.tb = 0; b.rg = 0; b.active = false;
+    b.wq = reinterpret_cast<const u32x4_t*>(p.wq);
+    b.ws = reinterpret_cast<const u32x2_t*>(p.wsc);
+    return b;
+  }
+  const int s = (int)(j / ((int64_t)js.P * js.Q));
+  const int rem = (int)(j - (int64_t)s * js.P * js.Q);
+  const int pass = rem / js.Q, quad = rem - pass * js.Q;
+  if constexpr (SET == SET_ROUTED) {
+    b.e = v;
+    b.slot0 = s * p.block;
+    b.count = p.block;
+  } else {
+    b.e = s;
+    b.slot0 = s * p.max_m;
+    b.count = v;
+  }
+  b.tb = pass * rows_per_pass;
+  const int rg_raw = quad * 4 + wave;
+  b.active = rg_raw < p.RG;
+  b.rg = b.active ? rg_raw : p.RG - 1;
+  const size_t tile0 = ((size_t)b.e * p.RG + b.rg) * p.Kc;
+  b.wq = reinterpret_cast<const u32x4_t*>(p.wq) + tile0 * (kMT * 64);
+  b.ws = reinterpret_cast<const u32x2_t*>(p.wsc) + tile0 * 64;
+  return b;
+}
+
+template <int SET>
+__device__ __forceinline__ Job make_job(const GemmParams& p, const JobSpace& js, int64_t j, int wave,
+                                        int rows_per_pass) {
+  const int v = j < js.j1 ? __builtin_amdgcn_readlane(js.info, (int)(j / ((int64_t)js.P * js.Q)) - js.s0)
+                          : 0;
+  return make_job_e<SET>(p, js, j, v, wave, rows_per_pass);
+}
+
+// The thread's token rows of a job (row 16*nt + thread/16 of its pass, pad
+// rows repeating the last row of the set): the slot, or with GATHER the flat
+// index stored there (a load whose value is first used a job later, in
+// row_ptr).
+template <int NT, bool GATHER>
+__device__ __forceinline__ void job_row_ids(const GemmParams& p, const Job& b, int (&id)[NT]) {
+  const int lr = threadIdx.x >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int slot = b.slot0 + min(b.tb + nt * 16 + lr, b.count - 1);
+    id[nt] = GATHER ? p.sorted_ids[slot] : slot;
+  }
+}
+
+template <int NT, bool GATHER>
+__device__ __forceinline__ void row_ptrs(const GemmParams& p, const int (&id)[NT],
+                                         const uint16_t* (&lrow)[NT]) {
+  const int lpiece = (threadIdx.x & 15) * 8;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    int row = id[nt];
+    if constexpr (GATHER) row = (row >= 0 && row < p.sentinel) ? row / p.topk : 0;   // pad: row 0
+    lrow[nt] = p.src + (size_t)row * p.src_ld + lpiece;
+  }
+}
+
+// Keeps a loaded value untouched until this point: the compiler may not
+// hoist its uses (and so the wait for the load) above it.
+__device__ __forceinline__ int pin(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Routing data of the lane's output rows (row 16*nt + lane%16 of the pass),
+// loaded when a job starts and first read by its epilogue: the slot's flat
+// index (routing blocks), or the row itself (masked; -1 past masked_m).
+template <int NT, int SET>
+__device__ __forceinline__ void job_epi_ids(const GemmParams& p, const Job& b, int lane, int (&f)[NT]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = b.tb + nt * 16 + (lane & 15);
+    if constexpr (SET == SET_ROUTED) {
+      f[nt] = p.sorted_ids[b.slot0 + min(r, b.count - 1)];   // r < count = block
+    } else {
+      f[nt] = r < b.count ? r : -1;
+    }
+  }
+}
+
+// Epilogue of one job from its prefetched routing data: pad slots and rows
+// past the set are skipped; SwiGLU and BF16 stores go to the row's slot,
+// weighted FP32 rows to its flat index.
+template <int NT, int SET, int EPI>
+__device__ __forceinline__ void job_epilogue(const GemmParams& p, const f32x4_t (&acc)[kMT][NT],
+                                             const Job& b, const int (&fid)[NT], int lane) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int f = pin(fid[nt]);
+    if (SET == SET_ROUTED ? (f < 0 || f >= p.sentinel) : f < 0) continue;
+    const int slot = b.slot0 + b.tb + nt * 16 + (lane & 15);
+    if constexpr (EPI == EPI_SWIGLU) {
+      uint16_t* dst = p.a_out + (size_t)slot * p.a_ld + b.rg * 32 + (lane >> 4) * 4;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const f32x4_t g = acc[2 * pp][nt], u = acc[2 * pp + 1][nt];
+        u32x2_t v;
+        v[0] = pack_bf16x2(swiglu(g[0], u[0]), swiglu(g[1], u[1]));
+        v[1] = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
+        *reinterpret_cast<u32x2_t*>(dst + pp * 16) = v;
+      }
+    } else if constexpr (EPI == EPI_COMBINE) {
+      const float w = p.topk_w[f];
+      float* dst = p.yrows + (size_t)f * p.yrows_ld;
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+        const int n = b.rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
+        if (n < p.N) *reinterpret_cast<f32x4_t*>(dst + n) = w * acc[mt][nt];
+      }
+    } else {
+      uint16_t* dst = p.out + (size_t)slot * p.out_ld;
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+        const int n = b.rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
+        if (n < p.N) {
+          u32x2_t v;
+          v[0] = pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]);
+          v[1] = pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]);
+          *reinterpret_cast<u32x2_t*>(dst + n) = v;
+        }
+      }
+    }
+  }
+}
+
+template <int NT, int SET, int EPI, bool DYN>
+__global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m_jobs(const GemmParams p) {
+  static_assert(!DYN || SET == SET_ROUTED, "the job queue serves routing blocks");
+  constexpr bool kGather = (SET == SET_ROUTED && EPI == EPI_SWIGLU);
+  constexpr int kRows = 16 * NT;
+  __shared__ TileLds<NT> lds;
+  __shared__ int qslot[4][2];   // DYN: jobs taken from the queue (index, expert)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // ---- this workgroup's job range
+  int nsets = p.nsets;
+  if constexpr (SET == SET_ROUTED) {
+    const int32_t* hdr = p.routing_hdr;
+    if (hdr[HDR_MAGIC] != kRoutingMagic || hdr[HDR_BLOCK] != p.block || hdr[HDR_E] != p.E ||
+        hdr[HDR_T] * hdr[HDR_TOPK] != p.sentinel)
+      return;   // routing made for other shapes: compute nothing
+    nsets = min(max(hdr[HDR_TOTAL], 0) / p.block, p.nsets);
+  }
+  JobSpace js;
+  js.P = p.passes;
+  js.Q = p.wg_per_set;
+  const int64_t per_set = (int64_t)js.P * js.Q;
+  const int64_t njobs = (int64_t)nsets * per_set;
+  Job cur, nxt, nx2;
+  int tk = 0;   // DYN: transitions so far (selects the queue slot)
+  if constexpr (DYN) {
+    // one thread takes jobs from the queue: index and the block's expert
+    auto take = [&](int slot) {
+      const int t = atomicAdd(p.queue, 1);
+      qslot[slot][0] = t;
+      qslot[slot][1] = t < njobs ? p.block_expert[t / per_set] : 0;
+    };
+    if (threadIdx.x == 0) {
+      take(0);
+      take(1);
+      take(2);
+      take(3);
+    }
+    __syncthreads();
+    js.s0 = 0;
+    js.j1 = njobs;
+    cur = make_job_e<SET>(p, js, qslot[0][0], qslot[0][1], wave, kRows);
+    nxt = make_job_e<SET>(p, js, qslot[1][0], qslot[1][1], wave, kRows);
+    nx2 = make_job_e<SET>(p, js, qslot[2][0], qslot[2][1], wave, kRows);
+    if (cur.j >= js.j1) return;
+  } else {
+    const int G = gridDim.x;
+    const int logical = xcd_remap(blockIdx.x, G);
+    const int64_t j0 = njobs * logical / G;
+    js.j1 = njobs * (logical + 1) / G;
+    if (j0 >= js.j1) return;
+    js.s0 = (int)(j0 / per_set);
+    if ((js.j1 - 1) / per_set - js.s0 >= 64) return;   // grid too small for the set table
+    {
+      const int s = js.s0 + lane;   // the range spans at most 64 sets (host-sized grid)
+      int v = -1;
+      if ((int64_t)s * per_set < js.j1) {
+        if constexpr (SET == SET_ROUTED) {
+          const int e = p.block_expert[s];
+          v = (e >= 0 && e < p.E) ? e : -1;
+        } else {
+          v = min(max(p.masked_m[s], 0), p.max_m);
+        }
+      }
+      js.info = v;
+    }
+    int64_t j = j0;
+    if (!job_valid<SET>(js, j, kRows)) j = next_job<SET>(js, j, kRows);
+    if (j >= js.j1) return;
+    cur = make_job<SET>(p, js, j, wave, kRows);
+    nxt = make_job<SET>(p, js, next_job<SET>(js, cur.j, kRows), wave, kRows);
+    nx2 = make_job<SET>(p, js, next_job<SET>(js, nxt.j, kRows), wave, kRows);
+  }
+  const uint16_t* lrow_cur[NT];
+  int id_nxt[NT];
+  {
+    int id_cur[NT];
+    job_row_ids<NT, kGather>(p, cur, id_cur);
+    row_ptrs<NT, kGather>(p, id_cur, lrow_cur);
+  }
+  job_row_ids<NT, kGather>(p, nxt, id_nxt);
+  int ef[NT];
+  job_epi_ids<NT, SET>(p, cur, lane, ef);
+
+  const int Kc = p.Kc;
+  const uint32_t mlo = kF16MagicLo, mhi = kF16MagicHi;
+  const int kmax = p.K - (threadIdx.x & 15) * 8;   // chunk kc is readable if kc*128 < kmax
+  constexpr int kCh = kMT * 64;                    // u32x4 per chunk of one row group
+
+  f32x4_t acc[kMT][NT];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: weights of the first two chunks of the stream, token tile of
+  // the first
+  AFrag fr0, fr1, fr2;
+  u32x4_t st[NT];
+  load_b<NT>(st, lrow_cur, 0, kmax);
+  load_a(fr0, cur.wq, cur.ws, lane);
+  if (Kc > 1)
+    load_a(fr1, cur.wq + kCh, cur.ws + 64, lane);
+  else
+    load_a(fr1, nxt.wq, nxt.ws, lane);
+  __syncthreads();
+  store_b<NT>(lds, 0, st);
+  __syncthreads();
+
+  int c = 0;   // chunk of the current job computed by the next step
+  bool live = true;
+  // step J computes chunk c of the current job from register buffer J and LDS
+  // buffer J, and prefetches the stream's next chunk of weights + 2 into
+  // register buffer (J+2)%3 and its next token chunk into LDS buffer (J+1)%3.
+  // A job's last chunk is followed by its epilogue and the shift to the next.
+#define MOE_JOB_STEP(J, CUR, NXT2)                                                            \
+  if (live) {                                                                                 \
+    {                                                                                         \
+      /* one load site each (selected addresses), so the waits stay where the */              \
+      /* data is consumed: tokens at the LDS store, weights two steps later */                 \
+      const bool tcur = c + 1 < Kc;                                                           \
+      const uint16_t* tp[NT];                                                                 \
+      if (tcur) {                                                                             \
+        _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) tp[nt] = lrow_cur[nt];              \
+      } else {                                                                                \
+        int idv[NT];                                                                          \
+        _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) idv[nt] = pin(id_nxt[nt]);          \
+        row_ptrs<NT, kGather>(p, idv, tp);                                                    \
+      }                                                                                       \
+      load_b<NT>(st, tp, tcur ? c + 1 : 0, kmax);                                             \
+      const int w2 = c + 2;                                                                   \
+      const bool wcur = w2 < Kc, wnxt = !wcur && w2 - Kc < Kc;                                \
+      const int wc = wcur ? w2 : (wnxt ? w2 - Kc : 0);                                        \
+      const u32x4_t* wqb = wcur ? cur.wq : (wnxt ? nxt.wq : nx2.wq);                          \
+      const u32x2_t* wsb = wcur ? cur.ws : (wnxt ? nxt.ws : nx2.ws);                          \
+      load_a(NXT2, wqb + (size_t)wc * kCh, wsb + (size_t)wc * 64, lane);                      \
+    }                                                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    mma_chunk<NT>(CUR, lds, J, acc, mlo, mhi);                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    if (++c == Kc) {                                                                          \
+      if (cur.active) job_epilogue<NT, SET, EPI>(p, acc, cur, ef, lane);                      \
+      _Pragma("unroll") for (int mt = 0; mt < kMT; ++mt)                                      \
+        _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f}; \
+      c = 0;                                                                                  \
+      cur = nxt;                                                                              \
+      nxt = nx2;                                                                              \
+      row_ptrs<NT, kGather>(p, id_nxt, lrow_cur);                                             \
+      job_row_ids<NT, kGather>(p, nxt, id_nxt);                                               \
+      job_epi_ids<NT, SET>(p, cur, lane, ef);                                                 \
+      if constexpr (DYN) {                                                                    \
+        /* the job taken at the previous transition; take the next one */                     \
+        const int sl = 3 - (tk & 1);                                                          \
+        nx2 = make_job_e<SET>(p, js, qslot[sl][0], qslot[sl][1], wave, kRows);                \
+        if (threadIdx.x == 0) {                                                               \
+          const int t = atomicAdd(p.queue, 1);                                                \
+          qslot[5 - sl][0] = t;                                                               \
+          qslot[5 - sl][1] = t < njobs ? p.block_expert[t / per_set] : 0;                     \
+        }                                                                                     \
+        ++tk;                                                                                 \
+      } else {                                                                                \
+        nx2 = make_job<SET>(p, js, next_job<SET>(js, nx2.j, kRows), wave, kRows);             \
+      }                                                                                       \
+      live = cur.j < js.j1;                                                                   \
+    }                                                                                         \
+    store_b<NT>(lds, (J + 1) % 3, st);                                                        \
+    __syncthreads();                                                                          \
+  }
+  while (live) {
+    MOE_JOB_STEP(0, fr0, fr2)
+    MOE_JOB_STEP(1, fr1, fr0)
+    MOE_JOB_STEP(2, fr2, fr1)
+  }
+#undef MOE_JOB_STEP
+}
+
+
 template <int NT>
 hipError_t launch_nt(const GemmParams& p, int set, int epi, hipStream_t s) {
   const dim3 grid(p.total_wg), block(256);
+  if (p.dispatch) {   // persistent forms: routing blocks of one weight pass
+    if (set != SET_ROUTED || (epi != EPI_SWIGLU && epi != EPI_COMBINE)) return hipErrorInvalidValue;
+    if (p.dispatch == 2 && !p.queue) return hipErrorInvalidValue;
+#define MOE_JOBS_CASE(EPI_, DYN_)                                                  \
+    if (epi == EPI_ && (p.dispatch == 2) == DYN_) {                                \
+      hipLaunchKernelGGL((gemm_small_m_jobs<NT, SET_ROUTED, EPI_, DYN_>), grid, block, 0, s, p); \
+      return hipGetLastError();                                                    \
+    }
+    MOE_JOBS_CASE(EPI_SWIGLU, false)
+    MOE_JOBS_CASE(EPI_SWIGLU, true)
+    MOE_JOBS_CASE(EPI_COMBINE, false)
+    MOE_JOBS_CASE(EPI_COMBINE, true)
+#undef MOE_JOBS_CASE
+    return hipErrorInvalidValue;
+  }
 #define MOE_GEMM_CASE(SET_, EPI_)                                                  \
   if (set == SET_ && epi == EPI_) {                                                \
     hipLaunchKernelGGL((gemm_small_m<NT, SET_, EPI_>), grid, block, 0, s, p);     \

@@ -30,6 +30,11 @@ struct GemmParams {
   int E, RG, Kc, K, N;   // N: true rows (output features)
   int wg_per_set;        // workgroups per row set: ceil(RG / 4), or ceil(ceil(RG / 4) / qpw)
   int qpw;               // large-M K-resident form (K <= 256): row-group quads per workgroup; 0 off
+  // small-M on routing blocks: 0 one workgroup per (expert, quad); 1 persistent
+  // workgroups, static job ranges; 2 persistent workgroups on the job queue
+  int dispatch;
+  int passes;            // persistent forms: token passes of 16*NT rows per routing block
+  int32_t* queue;        // dispatch 2: job counter, zero at launch
   int nsets;             // row sets (experts or blocks)
   int total_wg;
   // row sets
@@ -58,6 +63,8 @@ struct GemmParams {
   int64_t out_ld;             // STORE
 };
 
+// dispatch 1 or 2: routing blocks (SET_ROUTED, block 16*nt) only; total_wg
+// workgroups, enough that a static range spans at most 64 blocks.
 hipError_t launch_gemm_small_m(const GemmParams& p, int set, int epi, int nt, hipStream_t s);
 // K must be a multiple of 128; qpw > 0 (K-resident form) needs K <= 256 and
 // a routing or contiguous row set.
