@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=1,
                     help="index into synth.WORKLOADS (1: the Kimi decode layer, the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="indexed workloads: time the unfused steps (align, gate_up GEMM with a BF16 "
+                         "output, SwiGLU, down GEMM with a BF16 output; no combine) instead of the layer")
     ap.add_argument("--dispatch", type=int, default=0, choices=(0, 1, 2),
                     help="indexed small-M token-tile dispatch: 0 semi-static grid (default), "
                          "1 persistent static ranges, 2 persistent atomic job queue")
@@ -150,6 +153,10 @@ def main():
     import w4a16_int4_grouped_amd as M
 
     wl = synth.WORKLOADS[args.workload]
+    if args.unfused and wl.layout != "indexed":
+        print(f"--unfused runs the indexed layout's steps; workload {args.workload} is {wl.layout}",
+              file=sys.stderr)
+        sys.exit(2)
     log(f"workload {wl.name}: generating inputs")
     t = time.time()
     w = synth.stacked_weights(wl)
@@ -174,6 +181,19 @@ def main():
 
         def step():
             h.indexed(x_d, ids_d, tw_d, out=out, ws=ws, stream=stream, ovr=ovr)
+
+        if args.unfused:
+            lay = h.routing_layout(wl.T, wl.topk, ovr)
+            routing_buf = torch.empty(lay.total_ints, dtype=torch.int32, device="cuda")
+            hbuf = torch.empty((lay.cap, 2 * wl.I), dtype=torch.bfloat16, device="cuda")
+            abuf = torch.empty((lay.cap, wl.I), dtype=torch.bfloat16, device="cuda")
+            ybuf = torch.empty((lay.cap, wl.H), dtype=torch.bfloat16, device="cuda")
+
+            def step():
+                h.align(ids_d, ovr=ovr, routing=routing_buf, stream=stream)
+                h.gate_up(x_d, wl.topk, routing_buf, out=hbuf, ovr=ovr, stream=stream)
+                M.swiglu(hbuf, out=abuf, stream=stream)
+                h.down(abuf, wl.T, wl.topk, routing_buf, out=ybuf, ovr=ovr, stream=stream)
     elif wl.layout == "contiguous":
         # the contiguous input comes from the library's own align (block 128) + permute
         x = synth.activations(wl.iseed, wl.T, wl.H)
@@ -262,6 +282,8 @@ def main():
                    "intermediate": wl.I, "tokens": wl.T, "topk": wl.topk, "rows": rows,
                    "experts_touched": touched, "weights": "uint4 g32 bf16-scale",
                    "dispatch": ["semi-static", "persistent-static", "persistent-queue"][args.dispatch],
+                   "steps": "unfused: align, gate_up, swiglu, down (BF16 hand-offs, no combine)"
+                   if args.unfused else "fused layer",
                    "layer_packed_GBps": layer_packed / (ms * 1e-3) / 1e9,
                    "layer_packed_frac_hbm": layer_packed / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                    "layer_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,

@@ -285,6 +285,46 @@ moe_status_t moe_w4a16_masked(const moe_weights_t* h, const uint16_t* a3, int32_
                               void* ws, size_t ws_bytes, const moe_tuning_t* ovr,
                               moe_stream_t stream);
 
+/* ---- unfused steps (indexed layout) ---------------------------------------
+ *
+ * The layer split at the contract the Chord page times its grouped kernels
+ * on ("Grouped SM90 kernels" and "H200 prefill and TP8": routing, activation
+ * and communication outside the timed GEMMs): the two grouped GEMMs with BF16
+ * outputs, and the activation, as separate calls on the rows of a routing
+ * made by moe_align for the same (T, topk, ovr). The GEMMs use the schedule
+ * moe_w4a16_indexed would (ovr.dispatch aside: always the semi-static grid).
+ * These are BF16 hand-offs: h and y are rounded to BF16 between the steps,
+ * where the fused call keeps them in FP32.
+ *
+ * moe_w4a16_gate_up: for every routing slot s holding flat index
+ * f = t*topk + j of expert e, h_out[s][c] = bf16(x[t] . W13[e][c]) over
+ * c < 2I in the canonical W13 row order (gate rows [0, I), up rows [I, 2I)).
+ *   x        device bf16 [T, H]
+ *   routing  device routing buffer (required)
+ *   h_out    device bf16 [cap, 2I], cap from moe_routing_layout; rows of pad
+ *            slots are left unspecified
+ * moe_w4a16_down: y_out[s][n] = bf16(a[s] . W2[e][n]) for the same slots.
+ *   a        device bf16 [cap, I] in routing-slot order (moe_swiglu of h_out)
+ *   y_out    device bf16 [cap, H]
+ * Errors: INVALID_ARG (NULL or misaligned pointers: x/a/outputs 16 B,
+ * routing 4 B), MODE_MISMATCH, OVERRIDE_REJECTED, HIP. A routing made for
+ * other (E, block, T*topk) computes nothing. Nothing is enqueued on error. */
+moe_status_t moe_w4a16_gate_up(const moe_weights_t* h, const uint16_t* x, int32_t T, int32_t topk,
+                               const void* routing, uint16_t* h_out, const moe_tuning_t* ovr,
+                               moe_stream_t stream);
+moe_status_t moe_w4a16_down(const moe_weights_t* h, const uint16_t* a, int32_t T, int32_t topk,
+                            const void* routing, uint16_t* y_out, const moe_tuning_t* ovr,
+                            moe_stream_t stream);
+
+/* SwiGLU on BF16 rows (reading of the layer's activation, as in the fused
+ * W13 epilogue): a[r][c] = bf16(silu(g) * u) with g = h[r][c], u = h[r][I + c]
+ * widened to FP32 and silu(z) = z / (1 + exp(-z)), for r < rows, c < inter.
+ *   h  device bf16 [rows, 2*inter], a device bf16 [rows, inter], 16-byte
+ *   aligned; inter a positive multiple of 8.
+ * Errors: INVALID_ARG, HIP. Needs no weights handle. */
+moe_status_t moe_swiglu(const uint16_t* h, int64_t rows, int32_t inter, uint16_t* a,
+                        moe_stream_t stream);
+
 /* ---- inspection ------------------------------------------------------------ */
 
 /* Dequantise one expert's prepared matrix back to canonical order with the

@@ -218,6 +218,32 @@ def expert_ffn(x_rows_bits, w13_bits, w2_bits):
     return h, a_bits, y
 
 
+# --------------------------------------------------------------------------
+# Unfused steps with BF16 hand-offs (the GEMM-level contract the Chord page
+# times in "Grouped SM90 kernels" and "H200 prefill and TP8": routing,
+# activation and communication outside the GEMMs)
+# --------------------------------------------------------------------------
+
+def gate_up_rows(x_rows_bits, w13_bits) -> np.ndarray:
+    """First grouped GEMM with a BF16 output: bf16(x . W13^T), float64 dot
+    products rounded once. Columns follow W13's rows: gate [0, I), up
+    [I, 2I)."""
+    return bf16_round(bf16_to_f64(x_rows_bits) @ bf16_to_f64(w13_bits).T)
+
+
+def swiglu_rows(h_bits) -> np.ndarray:
+    """SwiGLU of BF16 rows [.., 2I]: a = bf16(silu(g) * u), g = h[:, :I] and
+    u = h[:, I:] widened exactly (as in expert_ffn, from BF16 inputs)."""
+    h = bf16_to_f64(h_bits)
+    I = h.shape[-1] // 2
+    return bf16_round(silu(h[..., :I]) * h[..., I:])
+
+
+def down_rows(a_bits, w2_bits) -> np.ndarray:
+    """Second grouped GEMM with a BF16 output: bf16(a . W2^T)."""
+    return bf16_round(bf16_to_f64(a_bits) @ bf16_to_f64(w2_bits).T)
+
+
 def _expert_weights(weights, e):
     if callable(weights):
         return weights(e)

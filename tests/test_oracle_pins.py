@@ -375,6 +375,73 @@ def test_layer_onehot_exact():
     pin_layer_onehot()
 
 
+def pin_unfused_onehot():
+    """The unfused steps on one-hot weights: every output of gate_up_rows and
+    down_rows is one BF16 input times a power of two (exact), and
+    swiglu_rows equals z * expit(z) * u (scipy's logistic function) rounded
+    once to BF16 by the exact-rational rounder above."""
+    from scipy.special import expit
+    E, H, I, T = 2, 64, 32, 6
+    w13_q, w13_s, w2_q, w2_s = _onehot_weights(E, H, I)
+    r = np.random.default_rng(5)
+    x = torch_bf16_bits(r.standard_normal((T, H)).astype(np.float32))
+    xv = np.vectorize(f_bf16)(x.astype(np.int64))
+    for e in range(E):
+        s1, s2 = 2.0 ** -e, 2.0 ** (e - 1)
+        h = O.gate_up_rows(x, O.dequant(w13_q[e], w13_s[e]))
+        hv = np.vectorize(f_bf16)(h.astype(np.int64))
+        assert np.array_equal(hv, s1 * xv[:, np.arange(2 * I) % H])
+        a = O.swiglu_rows(h)
+        g, u = hv[:, :I], hv[:, I:]
+        ref_a = np.vectorize(lambda v: bf16_nearest_exact(v))(g * expit(g) * u)
+        assert np.array_equal(np.vectorize(f_bf16)(a.astype(np.int64)),
+                              np.vectorize(f_bf16)(ref_a.astype(np.int64)))
+        y = O.down_rows(a, O.dequant(w2_q[e], w2_s[e]))
+        av = np.vectorize(f_bf16)(a.astype(np.int64))
+        assert np.array_equal(np.vectorize(f_bf16)(y.astype(np.int64)), s2 * av[:, np.arange(H) % I])
+    # closed forms: silu(0) = 0, a zero up half gives 0, silu(30) = 30 to within 2^-40
+    h = torch_bf16_bits(np.array([[0.0, 30.0, 1.5, 0.0]], dtype=np.float32))
+    a = np.vectorize(f_bf16)(O.swiglu_rows(h).astype(np.int64))
+    assert a[0, 0] == 0.0 and a[0, 1] == 0.0
+    h = torch_bf16_bits(np.array([[30.0, 2.0]], dtype=np.float32))
+    assert f_bf16(int(O.swiglu_rows(h)[0, 0])) == 60.0
+
+
+def test_unfused_steps_onehot():
+    pin_unfused_onehot()
+
+
+def pin_unfused_bruteforce():
+    """gate_up_rows / down_rows on tiny random inputs against exact rational
+    dot products rounded to the nearest BF16 by exact comparison."""
+    r = np.random.default_rng(9)
+    H, I, T = 32, 16, 3
+    words = r.integers(0, 2 ** 32, size=(2 * I, H // 8), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    scales = torch_bf16_bits((np.abs(r.standard_normal((2 * I, H // 32))) * 0.05 + 1e-3).astype(np.float32))
+    w = O.dequant(words, scales)
+    x = torch_bf16_bits(r.standard_normal((T, H)).astype(np.float32))
+    got = O.gate_up_rows(x, w)
+    wv = [[_bf16_val(int(b)) for b in row] for row in w]
+    for t in range(T):
+        xv = [_bf16_val(int(b)) for b in x[t]]
+        for n in range(2 * I):
+            exact = sum((xv[k] * wv[n][k] for k in range(H)), Fraction(0))
+            assert int(got[t, n]) == bf16_nearest_exact(exact), (t, n)
+    a = O.swiglu_rows(got)
+    w2 = w[:, :I]                            # any BF16 matrix [H', I] serves as W2
+    y = O.down_rows(a, w2)
+    w2v = [[_bf16_val(int(b)) for b in row] for row in w2]
+    for t in range(T):
+        av = [_bf16_val(int(b)) for b in a[t]]
+        for n in range(w2.shape[0]):
+            exact = sum((av[k] * w2v[n][k] for k in range(I)), Fraction(0))
+            assert int(y[t, n]) == bf16_nearest_exact(exact), (t, n)
+
+
+def test_unfused_steps_bruteforce():
+    pin_unfused_bruteforce()
+
+
 def pin_split_identity():
     """concat(h_i) . W^T = sum_i h_i . W_i^T with K split at multiples of 32
     (DFlash audit, section 2). Dequantising a K-slice of the packed words and
@@ -537,10 +604,21 @@ def _round_ties_away(x):
     return out
 
 
+def _swiglu_swapped(h_bits):
+    h = O.bf16_to_f64(h_bits)
+    I = h.shape[-1] // 2
+    return O.bf16_round(O.silu(h[..., I:]) * h[..., :I])
+
+
+def _gate_up_truncated(x_rows_bits, w13_bits):
+    v = O.bf16_to_f64(x_rows_bits) @ O.bf16_to_f64(w13_bits).T
+    return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
 ALIGN_ORIG = O.align
 PINS = [pin_bf16_vs_torch, pin_unpack_golden, pin_dequant_golden, pin_align_golden,
         pin_align_bruteforce, pin_layer_bruteforce, pin_layer_onehot, pin_split_identity,
-        pin_layout_equality]
+        pin_layout_equality, pin_unfused_onehot, pin_unfused_bruteforce]
 
 
 @pytest.mark.parametrize("name,attr,bad", [
@@ -551,6 +629,8 @@ PINS = [pin_bf16_vs_torch, pin_unpack_golden, pin_dequant_golden, pin_align_gold
     ("h rounded to bf16", "expert_ffn", _ffn_round_h),
     ("unstable align", "align", _align_unstable),
     ("bf16 ties away from zero", "bf16_round", _round_ties_away),
+    ("unfused SwiGLU halves swapped", "swiglu_rows", _swiglu_swapped),
+    ("unfused gate_up unrounded h truncated", "gate_up_rows", _gate_up_truncated),
 ])
 def test_planted_mistakes_are_caught(monkeypatch, name, attr, bad):
     monkeypatch.setattr(O, attr, bad)

@@ -39,7 +39,8 @@ EXPORTS = [
     "moe_abi_version", "moe_last_error", "moe_status_string", "moe_prepared_bytes",
     "moe_prepare_weights", "moe_release_weights", "moe_plan_create", "moe_routing_block", "moe_routing_bytes",
     "moe_routing_layout", "moe_align", "moe_permute", "moe_workspace_bytes", "moe_w4a16_indexed",
-    "moe_w4a16_contiguous", "moe_w4a16_masked", "moe_dequant_weights", "moe_describe",
+    "moe_w4a16_contiguous", "moe_w4a16_masked", "moe_w4a16_gate_up", "moe_w4a16_down", "moe_swiglu",
+    "moe_dequant_weights", "moe_describe",
     "moe_profile_enable", "moe_profile_reset", "moe_profile_read",
 ]
 
@@ -109,6 +110,9 @@ def lib() -> ctypes.CDLL:
         "moe_w4a16_indexed": (S, [P, P, I32, I32, P, P, P, P, P, SZ, ctypes.POINTER(Tuning), P]),
         "moe_w4a16_contiguous": (S, [P, P, I32, P, P, P, I32, I32, P, P, SZ, ctypes.POINTER(Tuning), P]),
         "moe_w4a16_masked": (S, [P, P, I32, P, I32, P, P, SZ, ctypes.POINTER(Tuning), P]),
+        "moe_w4a16_gate_up": (S, [P, P, I32, I32, P, P, ctypes.POINTER(Tuning), P]),
+        "moe_w4a16_down": (S, [P, P, I32, I32, P, P, ctypes.POINTER(Tuning), P]),
+        "moe_swiglu": (S, [P, I64, I32, P, P]),
         "moe_dequant_weights": (S, [P, I32, I32, P, P]),
         "moe_describe": (S, [P, I32, I32, I32, I32, ctypes.POINTER(Tuning), ctypes.c_char_p, SZ]),
         "moe_profile_enable": (S, [S]),
@@ -263,6 +267,27 @@ class PreparedWeights:
                                      _ptr(ws), ws.numel() * ws.element_size(), _tuning(ovr), _stream(stream)))
         return out
 
+    # -- unfused steps (indexed) ------------------------------------------------
+    def gate_up(self, x, topk, routing, out=None, ovr=None, stream=None):
+        """BF16 [cap, 2I] gate | up rows at the routing's slots."""
+        import torch
+        T = x.shape[0]
+        if out is None:
+            cap = self.routing_layout(T, topk, ovr).cap
+            out = torch.empty((cap, 2 * self.I), dtype=torch.bfloat16, device=self.device)
+        check(lib().moe_w4a16_gate_up(self.handle, _ptr(x), T, topk, _ptr(routing), _ptr(out), _tuning(ovr),
+                                      _stream(stream)))
+        return out
+
+    def down(self, a, T, topk, routing, out=None, ovr=None, stream=None):
+        """BF16 [cap, H] rows of the second GEMM at the routing's slots."""
+        import torch
+        if out is None:
+            out = torch.empty((a.shape[0], self.H), dtype=torch.bfloat16, device=self.device)
+        check(lib().moe_w4a16_down(self.handle, _ptr(a), T, topk, _ptr(routing), _ptr(out), _tuning(ovr),
+                                   _stream(stream)))
+        return out
+
     def dequant(self, which, expert, stream=None):
         import torch
         shape = (2 * self.I, self.H) if which == 13 else (self.H, self.I)
@@ -277,6 +302,16 @@ class PreparedWeights:
         if n < 0:
             raise MoeError(MOE_ERR_INVALID_ARG, last_error())
         return buf.value.decode()
+
+
+def swiglu(h, out=None, stream=None):
+    """BF16 [rows, I] = silu(h[:, :I]) * h[:, I:] for BF16 h [rows, 2I]."""
+    import torch
+    rows, two_i = h.shape
+    if out is None:
+        out = torch.empty((rows, two_i // 2), dtype=torch.bfloat16, device=h.device)
+    check(lib().moe_swiglu(_ptr(h), rows, two_i // 2, _ptr(out), _stream(stream)))
+    return out
 
 
 def profile_enable(on=True):

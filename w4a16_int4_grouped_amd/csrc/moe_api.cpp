@@ -732,6 +732,84 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   return ok();
 }
 
+// One grouped GEMM of the indexed layout with a BF16 output at routing-slot
+// rows (the unfused step sequence): mat 13 (x gathered through the routing,
+// output gate | up) or 2 (a rows at their slots).
+static moe_status_t indexed_gemm_step(const moe_weights_t* hc, int mat, const uint16_t* src, int32_t T,
+                               int32_t topk, const void* routing, uint16_t* out,
+                               const moe_tuning_t* ovr, moe_stream_t stream) {
+  moe_weights_t* h = const_cast<moe_weights_t*>(hc);
+  moe_status_t st = check_handle(h, MOE_MODE_INDEXED);
+  if (st != MOE_OK) return st;
+  if ((st = check_topk(h, T, topk)) != MOE_OK) return st;
+  if (ovr && ovr->schedule && (ovr->schedule < 0 || ovr->schedule > 2))
+    return fail(MOE_ERR_INVALID_ARG, "schedule override %d not in 0..2", ovr->schedule);
+  const int B = moe_routing_block(h, T, topk, ovr);
+  if (!B) return large_m_rejected(h, ovr) ? MOE_ERR_OVERRIDE_REJECTED : MOE_ERR_INVALID_ARG;
+  if (T == 0) return ok();
+  if (!src || !routing || !out) return fail(MOE_ERR_INVALID_ARG, "NULL input / routing / output");
+  if (!aligned(src, 16) || !aligned(out, 16) || !aligned(routing, 4))
+    return fail(MOE_ERR_INVALID_ARG, "misaligned pointer (input/output 16 B, routing 4 B)");
+  if ((st = set_device(h)) != MOE_OK) return st;
+  const Schedule sc = schedule_indexed(h, T, topk, ovr);
+  RoutingLayout R;
+  R.init(h->desc.num_experts, T, topk, B);
+  const int32_t* rt = (const int32_t*)routing;
+  const int H = h->desc.hidden, I = h->desc.inter, E = h->desc.num_experts;
+  GemmParams p{};
+  p.counts = rt + R.off_counts;
+  p.offsets = rt + R.off_offsets;
+  p.sorted_ids = rt + R.off_sorted;
+  p.routing_hdr = rt;
+  p.sentinel = T * topk;
+  p.topk = topk;
+  p.block = B;
+  p.block_expert = rt + R.off_block_expert;
+  const bool large = sc.kind == SCHED_LARGE_M;
+  p.nsets = large ? R.nblocks : E;
+  const int set = large ? SET_ROUTED : SET_INDEXED;
+  fill_weights(p, h, mat == 13 ? h->lay.w13 : h->lay.w2);
+  p.total_wg = p.nsets * p.wg_per_set;
+  p.src = src;
+  p.src_ld = mat == 13 ? H : I;
+  p.gather = mat == 13;
+  p.out = out;
+  p.out_ld = mat == 13 ? 2 * I : H;
+  p.gate_up_I = mat == 13 ? I : 0;
+  Schedule semi = sc;
+  semi.dispatch = 0;   // the persistent forms serve the fused call only
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = run_gemm(mat, semi, p, set, EPI_STORE, s, h->env);
+  if (e != hipSuccess) return hip_fail(e, mat == 13 ? "gate_up launch" : "down launch");
+  return ok();
+}
+
+moe_status_t moe_w4a16_gate_up(const moe_weights_t* h, const uint16_t* x, int32_t T, int32_t topk,
+                               const void* routing, uint16_t* h_out, const moe_tuning_t* ovr,
+                               moe_stream_t stream) {
+  return indexed_gemm_step(h, 13, x, T, topk, routing, h_out, ovr, stream);
+}
+
+moe_status_t moe_w4a16_down(const moe_weights_t* h, const uint16_t* a, int32_t T, int32_t topk,
+                            const void* routing, uint16_t* y_out, const moe_tuning_t* ovr,
+                            moe_stream_t stream) {
+  return indexed_gemm_step(h, 2, a, T, topk, routing, y_out, ovr, stream);
+}
+
+moe_status_t moe_swiglu(const uint16_t* h, int64_t rows, int32_t inter, uint16_t* a,
+                        moe_stream_t stream) {
+  if (rows < 0 || inter <= 0 || inter % 8)
+    return fail(MOE_ERR_INVALID_ARG, "rows %lld / inter %d (a positive multiple of 8)", (long long)rows,
+                inter);
+  if (rows == 0) return ok();
+  if (!h || !a || !aligned(h, 16) || !aligned(a, 16))
+    return fail(MOE_ERR_INVALID_ARG, "h / a NULL or not 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = run("swiglu", s, [&] { return launch_swiglu(h, rows, inter, a, s); });
+  if (e != hipSuccess) return hip_fail(e, "swiglu launch");
+  return ok();
+}
+
 moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, int32_t M_pad,
                                   const int32_t* m_indices, const int32_t* row_src,
                                   const float* topk_w, int32_t T, int32_t topk, uint16_t* out,

@@ -43,6 +43,27 @@ __global__ __launch_bounds__(256) void combine_rows(const f32x4_t* __restrict__ 
   out[(size_t)t * H4 + c] = r;
 }
 
+// Standalone SwiGLU of the unfused step sequence: one thread per (row, 8
+// columns); gate and up are the row's BF16 halves [0, I) and [I, 2I), each
+// widened exactly to FP32, and the product is rounded once to BF16 (the
+// same arithmetic as the fused W13 epilogue, from BF16 instead of FP32
+// inputs).
+__global__ __launch_bounds__(256) void swiglu_rows(const u32x4_t* __restrict__ h, int64_t rows,
+                                                   int I8, u32x4_t* __restrict__ a) {
+  const int64_t n = rows * I8;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / I8;
+    const int c = (int)(i - r * I8);
+    const u32x4_t g = __builtin_nontemporal_load(h + r * 2 * I8 + c);
+    const u32x4_t u = __builtin_nontemporal_load(h + r * 2 * I8 + I8 + c);
+    u32x4_t o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      o[k] = pack_bf16x2(swiglu(bf16_lo(g[k]), bf16_lo(u[k])), swiglu(bf16_hi(g[k]), bf16_hi(u[k])));
+    a[i] = o;
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_i32(int32_t* __restrict__ p, int n, int v) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = v;
@@ -66,6 +87,16 @@ __global__ __launch_bounds__(128) void contiguous_valid(const int32_t* __restric
 }
 
 }  // namespace
+
+hipError_t launch_swiglu(const uint16_t* h, int64_t rows, int I, uint16_t* a, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (I <= 0 || I % 8) return hipErrorInvalidValue;
+  const int64_t n = rows * (I / 8);
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(swiglu_rows, dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(256), 0, s,
+                     reinterpret_cast<const u32x4_t*>(h), rows, I / 8, reinterpret_cast<u32x4_t*>(a));
+  return hipGetLastError();
+}
 
 hipError_t launch_combine_rows(const float* yrows, const int32_t* valid, const int32_t* hdr, int E,
                                int block, int T, int topk, int H, uint16_t* out, hipStream_t s) {

@@ -146,6 +146,20 @@ __device__ __forceinline__ int wave_max(int v) {
   return v;
 }
 
+// Output column of a BF16 store epilogue for lane `lane` of MFMA tile mt of
+// row group rg (4 columns from the returned one), or -1 past the output.
+// A W13 store (gate_up_I = I) undoes the prepared gate/up interleave: tiles
+// 0, 2 of a row group are gate columns rg*32 + (0, 16), tiles 1, 3 the same
+// up columns, I further on.
+__device__ __forceinline__ int store_col(int N, int gate_up_I, int rg, int mt, int lane) {
+  if (gate_up_I) {
+    const int c = rg * 32 + (mt >> 1) * 16 + (lane >> 4) * 4;
+    return c < gate_up_I ? c + (mt & 1) * gate_up_I : -1;
+  }
+  const int n = rg * 64 + mt * 16 + (lane >> 4) * 4;
+  return n < N ? n : -1;
+}
+
 // SiLU(g) * u in FP32.
 __device__ __forceinline__ float swiglu(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;

@@ -153,7 +153,8 @@ struct TileCtx {
 template <int SET, int EPI>
 __device__ __forceinline__ void tile_sources(const GemmParams& p, const TileCtx& c, int tb,
                                              const char* (&src)[2]) {
-  constexpr bool kGather = (SET == SET_ROUTED && EPI == EPI_SWIGLU);
+  // rows of x gathered through the routing (W13 of the indexed layout)
+  const bool gather = SET == SET_ROUTED && p.gather;
   const int lane = c.lane;
   const int piece = dma_piece(lane);
 #pragma unroll
@@ -161,7 +162,7 @@ __device__ __forceinline__ void tile_sources(const GemmParams& p, const TileCtx&
     const int r = tb + 32 * c.wave + 16 * ql + (lane >> 2);   // tile row
     int row;
     if constexpr (SET == SET_ROUTED) {
-      if constexpr (kGather) {
+      if (gather) {
         const int f = p.sorted_ids[c.slot0 + r];
         row = (f >= 0 && f < p.sentinel) ? f / p.topk : 0;   // pad slots read row 0
       } else {
@@ -216,11 +217,15 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c, 
         if (n < p.N) *reinterpret_cast<f32x4_t*>(dst + n) = w * acc[mt][nt];
       }
     } else {
+      if constexpr (SET == SET_ROUTED) {
+        const int f = p.sorted_ids[slot];
+        if (f < 0 || f >= p.sentinel) continue;   // pad slot: output unspecified
+      }
       uint16_t* dst = p.out + (size_t)slot * p.out_ld;
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
-        const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
-        if (n < p.N) {
+        const int n = store_col(p.N, p.gate_up_I, rg, mt, lane);
+        if (n >= 0) {
           u32x2_t v;
           v[0] = pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]);
           v[1] = pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]);
@@ -290,8 +295,8 @@ __device__ __forceinline__ void epilogue_meta(const GemmParams& p, const TileCtx
       uint16_t* dst = p.out + (size_t)slot * p.out_ld;
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
-        const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
-        if (n < p.N) {
+        const int n = store_col(p.N, p.gate_up_I, rg, mt, lane);
+        if (n >= 0) {
           u32x2_t v;
           v[0] = pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]);
           v[1] = pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]);
@@ -499,6 +504,7 @@ hipError_t launch_gemm_large_m(const GemmParams& p, int set, int epi, hipStream_
   }
     MOE_GEMM_RES(SET_ROUTED, EPI_SWIGLU)
     MOE_GEMM_RES(SET_ROUTED, EPI_COMBINE)
+    MOE_GEMM_RES(SET_ROUTED, EPI_STORE)
     MOE_GEMM_RES(SET_BLOCKS, EPI_SWIGLU)
     MOE_GEMM_RES(SET_BLOCKS, EPI_COMBINE)
     MOE_GEMM_RES(SET_BLOCKS, EPI_STORE)
@@ -512,6 +518,7 @@ hipError_t launch_gemm_large_m(const GemmParams& p, int set, int epi, hipStream_
   }
   MOE_GEMM_CASE(SET_ROUTED, EPI_SWIGLU)
   MOE_GEMM_CASE(SET_ROUTED, EPI_COMBINE)
+  MOE_GEMM_CASE(SET_ROUTED, EPI_STORE)
   MOE_GEMM_CASE(SET_MASKED, EPI_SWIGLU)
   MOE_GEMM_CASE(SET_MASKED, EPI_STORE)
   MOE_GEMM_CASE(SET_BLOCKS, EPI_SWIGLU)

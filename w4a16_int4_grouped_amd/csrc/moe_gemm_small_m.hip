@@ -155,7 +155,8 @@ constexpr int kSmallMBlocksPerCU = NT == 1 ? 4 : (NT == 2 ? 3 : 2);
 
 template <int NT, int SET, int EPI>
 __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(const GemmParams p) {
-  constexpr bool kGather = (SET == SET_INDEXED && EPI == EPI_SWIGLU);
+  // rows of x gathered through the routing (W13 of the indexed layout)
+  const bool gather = SET == SET_INDEXED && p.gather;
   __shared__ TileLds<NT> lds;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
     for (int nt = 0; nt < NT; ++nt) {
       const int r = min(tb + nt * 16 + lr, count - 1);   // pad columns repeat a valid row
       const int slot = slot0 + r;
-      const int row = kGather ? p.sorted_ids[slot] / p.topk : slot;
+      const int row = gather ? p.sorted_ids[slot] / p.topk : slot;
       lrow[nt] = p.src + (size_t)row * p.src_ld + lpiece;
     }
     f32x4_t acc[kMT][NT];
@@ -289,8 +290,8 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
         uint16_t* dst = p.out + (size_t)slot * p.out_ld;
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
-          const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
-          if (n < p.N) {
+          const int n = store_col(p.N, p.gate_up_I, rg, mt, lane);
+          if (n >= 0) {
             u32x2_t v;
             v[0] = pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]);
             v[1] = pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]);
@@ -481,8 +482,8 @@ __device__ __forceinline__ void job_epilogue(const GemmParams& p, const f32x4_t 
       uint16_t* dst = p.out + (size_t)slot * p.out_ld;
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
-        const int n = b.rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
-        if (n < p.N) {
+        const int n = store_col(p.N, p.gate_up_I, b.rg, mt, lane);
+        if (n >= 0) {
           u32x2_t v;
           v[0] = pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]);
           v[1] = pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]);
@@ -696,6 +697,7 @@ hipError_t launch_nt(const GemmParams& p, int set, int epi, hipStream_t s) {
   }
   MOE_GEMM_CASE(SET_INDEXED, EPI_SWIGLU)
   MOE_GEMM_CASE(SET_INDEXED, EPI_COMBINE)
+  MOE_GEMM_CASE(SET_INDEXED, EPI_STORE)
   MOE_GEMM_CASE(SET_MASKED, EPI_SWIGLU)
   MOE_GEMM_CASE(SET_MASKED, EPI_STORE)
   MOE_GEMM_CASE(SET_BLOCKS, EPI_SWIGLU)

@@ -20,7 +20,7 @@ enum RowSet : int {
 enum Epilogue : int {
   EPI_SWIGLU = 0,    // W13: a[slot][c] = bf16(silu(gate) * up)
   EPI_COMBINE = 1,   // W2: yrows[f][n] = w[f] * y   (f from sorted_ids / row_src)
-  EPI_STORE = 2,     // W2: out[slot][n] = bf16(y)
+  EPI_STORE = 2,     // out[slot][n] = bf16(y); W13 with gate_up_I: gate columns [0, I), up [I, 2I)
 };
 
 struct GemmParams {
@@ -61,6 +61,7 @@ struct GemmParams {
   int64_t yrows_ld;           // COMBINE: weighted rows, one per flat index f
   uint16_t* out;
   int64_t out_ld;             // STORE
+  int gate_up_I;              // STORE of W13 (gate_up_I = I): un-interleave gate | up columns
 };
 
 // dispatch 1 or 2: routing blocks (SET_ROUTED, block 16*nt) only; total_wg
@@ -69,6 +70,10 @@ hipError_t launch_gemm_small_m(const GemmParams& p, int set, int epi, int nt, hi
 // K must be a multiple of 128; qpw > 0 (K-resident form) needs K <= 256 and
 // a routing or contiguous row set.
 hipError_t launch_gemm_large_m(const GemmParams& p, int set, int epi, hipStream_t s);
+
+// a[r][c] = bf16(silu(h[r][c]) * h[r][I + c]) for r < rows, c < I (I a
+// multiple of 8; h rows of 2I, a rows of I, BF16).
+hipError_t launch_swiglu(const uint16_t* h, int64_t rows, int I, uint16_t* a, hipStream_t s);
 
 hipError_t launch_align(const int32_t* topk_ids, int T, int topk, int E, const RoutingLayout& L,
                         int32_t* routing, hipStream_t s);
