@@ -174,13 +174,28 @@ def main():
         x_d, ids_d, tw_d = to_dev(x, torch, np), to_dev(ids, torch, np), to_dev(tw, torch, np)
         out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
         ovr = {"dispatch": args.dispatch} if args.dispatch else None
+        Eg = wl.extra.get("global_experts", 0)
+        if Eg:   # expert-parallel share: experts 0 .. E-1 of the Eg global ones
+            ovr = dict(ovr or {}, global_experts=Eg)
+            emap = np.full(Eg, -1, dtype=np.int32)
+            emap[:wl.E] = np.arange(wl.E)
+            map_d = to_dev(emap, torch, np)
+            ids = np.where((ids >= 0) & (ids < wl.E), ids, -1)   # the share's rows, for the counts
         ws = torch.empty(h.workspace_bytes(wl.T, wl.topk, wl.T, ovr=ovr), dtype=torch.uint8, device="cuda")
         log(f"  schedule: {h.describe(wl.T, wl.topk, ovr=ovr)}")
-        rows = wl.T * wl.topk
+        rows = int(((ids >= 0) & (ids < wl.E)).sum())
         touched = int(np.unique(ids[(ids >= 0) & (ids < wl.E)]).size)
 
         def step():
             h.indexed(x_d, ids_d, tw_d, out=out, ws=ws, stream=stream, ovr=ovr)
+
+        if Eg:
+            routing_ep = torch.empty(h.routing_layout(wl.T, wl.topk, ovr).total_ints, dtype=torch.int32,
+                                     device="cuda")
+
+            def step():
+                h.align_ep(ids_d, map_d, Eg, ovr=ovr, routing=routing_ep, stream=stream)
+                h.indexed(x_d, ids_d, tw_d, routing=routing_ep, out=out, ws=ws, stream=stream, ovr=ovr)
 
         if args.unfused:
             lay = h.routing_layout(wl.T, wl.topk, ovr)
@@ -194,6 +209,20 @@ def main():
                 h.gate_up(x_d, wl.topk, routing_buf, out=hbuf, ovr=ovr, stream=stream)
                 M.swiglu(hbuf, out=abuf, stream=stream)
                 h.down(abuf, wl.T, wl.topk, routing_buf, out=ybuf, ovr=ovr, stream=stream)
+    elif wl.layout == "contiguous" and wl.extra.get("rows_per_expert"):
+        # grouped rows already aligned per expert (an EP share after its dispatch); no combine
+        rpe = wl.extra["rows_per_expert"]
+        total = wl.E * rpe
+        a_d = to_dev(synth.activations(wl.iseed, total, wl.H), torch, np)
+        m_d = to_dev(np.repeat(np.arange(wl.E, dtype=np.int32), rpe), torch, np)
+        out = torch.empty((total, wl.H), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(h.workspace_bytes(total, 0, 0), dtype=torch.uint8, device="cuda")
+        log(f"  M_pad={total}; schedule: {h.describe(total)}")
+        rows = total
+        touched = wl.E
+
+        def step():
+            h.contiguous(a_d, m_d, out=out, ws=ws, stream=stream)
     elif wl.layout == "contiguous":
         # the contiguous input comes from the library's own align (block 128) + permute
         x = synth.activations(wl.iseed, wl.T, wl.H)

@@ -107,7 +107,9 @@ typedef struct {
   int32_t block_m;  /* alignment block (rows): 16, 32, 64 or 128 */
   int32_t schedule; /* 0 auto, 1 small-M (decode), 2 large-M (prefill) */
   int32_t dispatch; /* small-M token-tile dispatch: 0, 1 or 2 (above) */
-  int32_t reserved1;
+  int32_t global_experts; /* expert parallelism: experts the routing is drawn
+                             from (0: the handle's); rows per expert, which pick
+                             the schedule, are T*topk / global_experts */
 } moe_tuning_t;
 
 typedef struct moe_weights moe_weights_t; /* opaque host handle */
@@ -210,6 +212,22 @@ moe_status_t moe_routing_layout(const moe_weights_t* h, int32_t T, int32_t topk,
 moe_status_t moe_align(const moe_weights_t* h, const int32_t* topk_ids, int32_t T, int32_t topk,
                        const moe_tuning_t* ovr, void* routing, size_t routing_bytes,
                        moe_stream_t stream);
+
+/* Alignment for one GPU's share of the experts (expert parallelism: the
+ * handle holds E of num_global_experts experts). topk_ids hold global ids;
+ * expert_map (device int32 [num_global_experts]) gives the handle's local
+ * expert for each global id, or -1 for an expert held elsewhere. Rows routed
+ * elsewhere are dropped as ids outside [0, E) are: they take no slot, so the
+ * indexed call given this routing adds only local experts' rows, and a token
+ * with none gets 0 (the partial output an EP combine sums over GPUs).
+ * Bit-exact; the same buffer layout, capacity and ovr rules as moe_align (set
+ * ovr.global_experts = num_global_experts for the schedule of the share).
+ * Errors: as moe_align, and INVALID_ARG for a NULL or misaligned map or
+ * num_global_experts outside 1..2^20. */
+moe_status_t moe_align_ep(const moe_weights_t* h, const int32_t* topk_ids, int32_t T, int32_t topk,
+                          const int32_t* expert_map, int32_t num_global_experts,
+                          const moe_tuning_t* ovr, void* routing, size_t routing_bytes,
+                          moe_stream_t stream);
 
 /* Gather x rows into the aligned order (the contiguous layout's producer):
  *   a_out      device bf16 [cap, H]: row p = x[sorted_ids[p] / topk], zero

@@ -150,6 +150,19 @@ def align(topk_ids, E: int, block: int) -> dict:
                 total=int(offsets[E]), cap=int(cap), block=int(block), sentinel=int(n))
 
 
+def ep_local_ids(topk_ids, expert_map) -> np.ndarray:
+    """Routing ids of one GPU's share of the experts under expert parallelism
+    (the grouped backend's H200 EP8 scope, Chord page, "Grouped SM90
+    kernels"): a global id g in [0, len(expert_map)) becomes expert_map[g],
+    the share's local expert or -1 for one held elsewhere; any other id
+    becomes -1. Rows with -1 contribute nothing, as ids outside [0, E) do.
+    """
+    ids = np.asarray(topk_ids).astype(np.int64)
+    m = np.asarray(expert_map).astype(np.int64)
+    ok = (ids >= 0) & (ids < m.size)
+    return np.where(ok, m[np.clip(ids, 0, max(m.size - 1, 0))], -1).astype(np.int32)
+
+
 def permute(x_bits, al: dict, topk: int) -> np.ndarray:
     """Gather activation rows into the sorted, padded order of an alignment.
 

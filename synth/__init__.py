@@ -68,6 +68,16 @@ WORKLOADS = {
     4: Workload("kimi-tp8-shard-indexed-e384-h7168-i256-t4096-top8", "indexed",
                 E=384, H=7168, I=256, T=4096, topk=8, routing="softmax",
                 wseed=104, iseed=204),
+    # one GPU's EP8 share (experts 0..47 of the 384, the decode workload's
+    # weights and routing); the routing draws global ids
+    5: Workload("kimi-ep8-share-decode-indexed-e48of384-h7168-i2048-t448-top8", "indexed",
+                E=48, H=7168, I=2048, T=448, topk=8, routing="softmax",
+                wseed=101, iseed=201, extra={"global_experts": 384}),
+    # one GPU's EP8 share at prefill: its 48 experts' rows after the dispatch,
+    # grouped and aligned, 512 rows per expert
+    6: Workload("kimi-ep8-share-prefill-contiguous-e48-h7168-i2048-512rows-per-expert", "contiguous",
+                E=48, H=7168, I=2048, T=0, topk=0, routing="none",
+                wseed=101, iseed=206, extra={"rows_per_expert": 512}),
 }
 
 
@@ -177,10 +187,13 @@ def zipf_routing(seed: int, T: int, E: int, topk: int, s: float = 1.1):
 
 
 def routing(w: Workload):
+    """Token routing of a workload: ids over its experts, or over the global
+    pool of an expert-parallel share (extra["global_experts"])."""
+    E = w.extra.get("global_experts", w.E)
     if w.routing == "softmax":
-        return softmax_routing(w.iseed, w.T, w.E, w.topk)
+        return softmax_routing(w.iseed, w.T, E, w.topk)
     if w.routing == "zipf":
-        return zipf_routing(w.iseed, w.T, w.E, w.topk, w.extra.get("zipf_s", 1.1))
+        return zipf_routing(w.iseed, w.T, E, w.topk, w.extra.get("zipf_s", 1.1))
     raise ValueError(f"workload {w.name} has no token routing")
 
 

@@ -99,6 +99,47 @@ def test_align_bit_exact(handles, name, E, T, topk, kind, block_m):
     assert got["total"] == ref["total"]
 
 
+EP_CASES = [
+    # (Eg, E_local, T, topk, placement, kind): one GPU's share of Eg experts
+    (384, 48, 448, 8, "contiguous", "softmax"),      # EP8 share of the decode routing
+    (384, 48, 448, 8, "round-robin", "softmax"),
+    (384, 48, 6000, 8, "round-robin", "zipf"),       # multi-workgroup path (48000 rows)
+    (16, 5, 37, 3, "contiguous", "softmax"),
+]
+
+
+def ep_map(Eg, E_local, placement, g=1):
+    emap = np.full(Eg, -1, dtype=np.int32)
+    if placement == "contiguous":
+        mine = np.arange(g * E_local, (g + 1) * E_local)
+    else:
+        mine = np.arange(g, Eg, Eg // E_local)[:E_local]
+    emap[mine] = np.arange(mine.size)
+    return emap
+
+
+@pytest.mark.parametrize("Eg,E,T,topk,placement,kind", EP_CASES)
+@pytest.mark.parametrize("block_m", [0, 128])
+def test_align_ep_bit_exact(handles, Eg, E, T, topk, placement, kind, block_m):
+    """Expert-parallel alignment: global ids through the share's map."""
+    h = handles(E)
+    ids = routing_ids(Eg, T, topk, kind, seed=300 + T).copy()
+    ids[::13, 0] = -1
+    ids[3 % T, topk - 1] = Eg + 2
+    emap = ep_map(Eg, E, placement)
+    ovr = {"global_experts": Eg}
+    if block_m:
+        ovr["block_m"] = block_m
+    routing = h.align_ep(i32_dev(ids), i32_dev(emap), Eg, ovr=ovr)
+    got = read_routing(h, routing, T, topk, ovr)
+    ref = O.align(O.ep_local_ids(ids, emap), E, got["block"])
+    log(f"  align_ep Eg={Eg} E={E} T={T} {placement} B={got['block']} total={ref['total']}")
+    for k in ("counts", "offsets", "sorted_ids", "block_expert"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert np.array_equal(got["slot_of"], slot_of_ref(ref))
+    assert got["total"] == ref["total"]
+
+
 def test_align_empty(handles):
     import torch
     h = handles(8)

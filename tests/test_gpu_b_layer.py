@@ -247,3 +247,31 @@ def test_indexed_small_dispatch(E, H, I, T, topk, wgs, dispatch, monkeypatch):
     # the same call again: the queue is cleared by each call
     out2 = h.indexed(bf16_dev(x), ids_d, f32_dev(tw), routing=routing, ws=ws, ovr=ovr)
     assert np.array_equal(bits_host(out2), bits_host(out))
+
+
+@pytest.mark.parametrize("Eg,E,H,I,T,topk,placement", [
+    (64, 8, 256, 128, 200, 8, "contiguous"),     # decode-like share: ~25 local rows per expert
+    (64, 8, 256, 128, 200, 8, "round-robin"),
+    (32, 4, 256, 256, 640, 4, "contiguous"),     # prefill-like share: ~80 rows per expert (large-M)
+])
+def test_indexed_ep_share(Eg, E, H, I, T, topk, placement):
+    """The layer on one GPU's expert share: only local rows are summed, tokens
+    with no local expert get 0 (the partial output of an EP combine)."""
+    require_gpu()
+    from tests.test_gpu_a_kernels import ep_map
+    log(f"case ep-share Eg={Eg} E={E} H={H} I={I} T={T} topk={topk} {placement}")
+    w = tiny_weights(E, H, I, seed=Eg + E)
+    x = synth.activations(51, T, H)
+    ids, tw = synth.softmax_routing(52, T, Eg, topk)
+    emap = ep_map(Eg, E, placement)
+    ovr = {"global_experts": Eg}
+    h = prepare(w, "indexed")
+    log(f"  {h.describe(T, topk, ovr=ovr)}")
+    routing = h.align_ep(i32_dev(ids), i32_dev(emap), Eg, ovr=ovr)
+    out = O.bf16_to_f64(bits_host(h.indexed(bf16_dev(x), i32_dev(ids), f32_dev(tw), routing=routing,
+                                            ovr=ovr)))
+    loc = O.ep_local_ids(ids, emap)
+    ref = O.moe_indexed(x, loc, tw, w, E=E)
+    none = np.all(loc < 0, axis=1)
+    assert np.all(out[none] == 0)
+    check_tol(out, ref, "indexed EP share")

@@ -1,4 +1,4 @@
-"""Full-size parity: the five workloads at their real shapes, run on the GPU
+"""Full-size parity: the workloads at their real shapes, run on the GPU
 exactly as the benchmark runs them, checked against the CPU oracle on
 sampled tokens / experts (the oracle recomputes those from the same seeded
 inputs). The contiguous result is compared with the oracle's indexed result
@@ -99,6 +99,63 @@ def test_full_prefill_contiguous(kimi):
     sample = np.array([0, wl.T - 1])
     ref = O.moe_indexed(x, ids, tw, _provider(w), E=wl.E, tokens=sample)
     check_tol(outf[sample], ref, f"{wl.name} tokens {sample.tolist()}")
+    del h
+
+
+def test_full_ep8_share_decode(kimi):
+    """One GPU's EP8 share of the decode workload: experts 0..47 of the 384
+    (the same weights), global ids through the share's map."""
+    import torch
+    _, w, _ = kimi
+    wl = synth.WORKLOADS[5]
+    Eg = wl.extra["global_experts"]
+    log(f"case {wl.name}")
+    ws = tuple(a[:wl.E] for a in w)
+    h = prepare(ws, "indexed")
+    x = synth.activations(wl.iseed, wl.T, wl.H)
+    ids, tw = synth.routing(wl)
+    emap = np.full(Eg, -1, dtype=np.int32)
+    emap[:wl.E] = np.arange(wl.E)
+    ovr = {"global_experts": Eg}
+    log(f"  {h.describe(wl.T, wl.topk, ovr=ovr)}")
+    routing = h.align_ep(i32_dev(ids), i32_dev(emap), Eg, ovr=ovr)
+    out = O.bf16_to_f64(bits_host(h.indexed(bf16_dev(x), i32_dev(ids), f32_dev(tw), routing=routing,
+                                            ovr=ovr)))
+    torch.cuda.synchronize()
+    loc = O.ep_local_ids(ids, emap)
+    has = np.flatnonzero(np.any(loc >= 0, axis=1))
+    none = np.flatnonzero(np.all(loc < 0, axis=1))
+    assert np.all(out[none] == 0)
+    sample = np.array([has[0], has[len(has) // 2], has[-1]])
+    ref = O.moe_indexed(x, loc, tw, _provider(ws), E=wl.E, tokens=sample)
+    check_tol(out[sample], ref, f"{wl.name} tokens {sample.tolist()}")
+    del h
+
+
+def test_full_ep8_share_prefill_grouped(kimi):
+    """One GPU's EP8 share at prefill: 48 experts x 512 aligned grouped rows
+    (contiguous layout, no combine), checked on sampled experts' rows."""
+    import torch
+    _, w, _ = kimi
+    wl = synth.WORKLOADS[6]
+    rpe = wl.extra["rows_per_expert"]
+    log(f"case {wl.name}")
+    ws = tuple(a[:wl.E] for a in w)
+    h = prepare(ws, "contiguous")
+    total = wl.E * rpe
+    a = synth.activations(wl.iseed, total, wl.H)
+    m_idx = np.repeat(np.arange(wl.E, dtype=np.int32), rpe)
+    log(f"  {h.describe(total)}")
+    out = h.contiguous(bf16_dev(a), i32_dev(m_idx))
+    torch.cuda.synchronize()
+    prov = _provider(ws)
+    for e in (0, wl.E - 1):
+        rows = np.arange(e * rpe, e * rpe + rpe)[::37]
+        w13 = O.dequant(*prov(e)[:2])
+        w2 = O.dequant(*prov(e)[2:])
+        _, _, y = O.expert_ffn(a[rows], w13, w2)
+        got = O.bf16_to_f64(bits_host(out[torch.from_numpy(rows).cuda()]))
+        check_tol(got, y, f"{wl.name} expert {e} rows {rows[:3].tolist()}..")
     del h
 
 

@@ -442,6 +442,37 @@ def test_unfused_steps_bruteforce():
     pin_unfused_bruteforce()
 
 
+def pin_ep_shards():
+    """Expert parallelism: the global id -> local id map agrees with a
+    brute-force loop, and the layer outputs of disjoint shards (contiguous
+    and round-robin placements of 8 experts over 4 GPUs) sum to the
+    unsharded layer (float64; only the order of additions differs)."""
+    x, ids, tw, (w13_q, w13_s, w2_q, w2_s) = _tiny_problem(H=64, I=32, E=8, T=9, k=3)
+    ids = ids.copy()
+    ids[2, 1] = -1
+    ids[5, 0] = 11                                # outside the global pool
+    full = O.moe_indexed(x, ids, tw, (w13_q, w13_s, w2_q, w2_s), E=8)
+    for place in ([0, 0, 1, 1, 2, 2, 3, 3], [0, 1, 2, 3, 0, 1, 2, 3]):
+        total = np.zeros_like(full)
+        for g in range(4):
+            mine = [e for e in range(8) if place[e] == g]
+            emap = np.full(8, -1, dtype=np.int32)
+            emap[mine] = np.arange(len(mine))
+            loc = O.ep_local_ids(ids, emap)
+            for t in range(ids.shape[0]):
+                for j in range(ids.shape[1]):
+                    gid = int(ids[t, j])
+                    want = int(emap[gid]) if 0 <= gid < 8 else -1
+                    assert int(loc[t, j]) == want
+            sub = tuple(a[mine] for a in (w13_q, w13_s, w2_q, w2_s))
+            total += O.moe_indexed(x, loc, tw, sub, E=len(mine))
+        np.testing.assert_allclose(total, full, rtol=1e-12, atol=1e-12 * np.abs(full).max())
+
+
+def test_ep_shards_sum_to_the_layer():
+    pin_ep_shards()
+
+
 def pin_split_identity():
     """concat(h_i) . W^T = sum_i h_i . W_i^T with K split at multiples of 32
     (DFlash audit, section 2). Dequantising a K-slice of the packed words and
@@ -618,7 +649,7 @@ def _gate_up_truncated(x_rows_bits, w13_bits):
 ALIGN_ORIG = O.align
 PINS = [pin_bf16_vs_torch, pin_unpack_golden, pin_dequant_golden, pin_align_golden,
         pin_align_bruteforce, pin_layer_bruteforce, pin_layer_onehot, pin_split_identity,
-        pin_layout_equality, pin_unfused_onehot, pin_unfused_bruteforce]
+        pin_layout_equality, pin_unfused_onehot, pin_unfused_bruteforce, pin_ep_shards]
 
 
 @pytest.mark.parametrize("name,attr,bad", [

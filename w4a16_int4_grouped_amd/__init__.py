@@ -38,7 +38,7 @@ MOE_PACK_INT32_LOW_NIBBLE_FIRST_K = 1
 EXPORTS = [
     "moe_abi_version", "moe_last_error", "moe_status_string", "moe_prepared_bytes",
     "moe_prepare_weights", "moe_release_weights", "moe_plan_create", "moe_routing_block", "moe_routing_bytes",
-    "moe_routing_layout", "moe_align", "moe_permute", "moe_workspace_bytes", "moe_w4a16_indexed",
+    "moe_routing_layout", "moe_align", "moe_align_ep", "moe_permute", "moe_workspace_bytes", "moe_w4a16_indexed",
     "moe_w4a16_contiguous", "moe_w4a16_masked", "moe_w4a16_gate_up", "moe_w4a16_down", "moe_swiglu",
     "moe_dequant_weights", "moe_describe",
     "moe_profile_enable", "moe_profile_reset", "moe_profile_read",
@@ -59,7 +59,7 @@ def make_desc(E, H, I, mode="indexed", bits=4, group_size=32, zero_point=8,
 
 class Tuning(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int32), ("schedule", ctypes.c_int32),
-                ("dispatch", ctypes.c_int32), ("reserved1", ctypes.c_int32)]
+                ("dispatch", ctypes.c_int32), ("global_experts", ctypes.c_int32)]
 
 
 class RoutingLayout(ctypes.Structure):
@@ -105,6 +105,7 @@ def lib() -> ctypes.CDLL:
         "moe_routing_bytes": (SZ, [P, I32, I32, ctypes.POINTER(Tuning)]),
         "moe_routing_layout": (S, [P, I32, I32, ctypes.POINTER(Tuning), ctypes.POINTER(RoutingLayout)]),
         "moe_align": (S, [P, P, I32, I32, ctypes.POINTER(Tuning), P, SZ, P]),
+        "moe_align_ep": (S, [P, P, I32, I32, P, I32, ctypes.POINTER(Tuning), P, SZ, P]),
         "moe_permute": (S, [P, P, I32, I32, ctypes.POINTER(Tuning), P, P, P, P, P]),
         "moe_workspace_bytes": (SZ, [P, I32, I32, I32, I32, ctypes.POINTER(Tuning)]),
         "moe_w4a16_indexed": (S, [P, P, I32, I32, P, P, P, P, P, SZ, ctypes.POINTER(Tuning), P]),
@@ -156,7 +157,7 @@ def _tuning(ovr):
     if isinstance(ovr, Tuning):
         return ctypes.byref(ovr)
     return ctypes.byref(Tuning(int(ovr.get("block_m", 0)), int(ovr.get("schedule", 0)),
-                               int(ovr.get("dispatch", 0)), 0))
+                               int(ovr.get("dispatch", 0)), int(ovr.get("global_experts", 0))))
 
 
 def _empty(nbytes, device):
@@ -212,6 +213,21 @@ class PreparedWeights:
             routing = torch.empty(nbytes // 4, dtype=torch.int32, device=self.device)
         check(lib().moe_align(self.handle, _ptr(topk_ids), T, topk, _tuning(ovr), _ptr(routing),
                               routing.numel() * routing.element_size(), _stream(stream)))
+        return routing
+
+    def align_ep(self, topk_ids, expert_map, num_global_experts, ovr=None, routing=None, stream=None):
+        """Routing of this handle's share of num_global_experts experts:
+        expert_map[global id] = local expert or -1."""
+        import torch
+        T, topk = topk_ids.shape
+        nbytes = lib().moe_routing_bytes(self.handle, T, topk, _tuning(ovr))
+        if nbytes == 0:
+            check(MOE_ERR_INVALID_ARG)
+        if routing is None:
+            routing = torch.empty(nbytes // 4, dtype=torch.int32, device=self.device)
+        check(lib().moe_align_ep(self.handle, _ptr(topk_ids), T, topk, _ptr(expert_map), num_global_experts,
+                                 _tuning(ovr), _ptr(routing), routing.numel() * routing.element_size(),
+                                 _stream(stream)))
         return routing
 
     def permute(self, x, topk, routing, ovr=None, stream=None):

@@ -53,23 +53,28 @@ __device__ __forceinline__ uint64_t match_peers(int e, int nbits) {
 // Key bits for experts 0 .. E-1 plus "none".
 __device__ __forceinline__ int key_bits(int E) { return 32 - __builtin_clz((unsigned)E); }
 
+// The local expert of flat row f: its id, or with an expert map (one GPU's
+// share of Eg global experts) map[id]; -1 when the row has no expert here.
+__device__ __forceinline__ int local_expert(const int32_t* __restrict__ ids, int f,
+                                            const int32_t* __restrict__ map, int Eg, int E) {
+  int e = ids[f];
+  if (map) e = (e >= 0 && e < Eg) ? map[e] : -1;
+  return (e >= 0 && e < E) ? e : -1;
+}
+
 // Places flat rows [lo, hi) stably. next[e] (LDS) holds expert e's next free
 // slot and is advanced; cnt (LDS, NWAVES x E) must be zero on entry and is
 // zero on exit. Called by all NWAVES*64 threads of the workgroup.
 template <int NWAVES>
-__device__ void place_rows(const int32_t* __restrict__ ids, int lo, int hi, int E,
-                           int32_t* next, int32_t* cnt, int32_t* __restrict__ sorted_ids,
-                           int32_t* __restrict__ slot_of) {
+__device__ void place_rows(const int32_t* __restrict__ ids, const int32_t* __restrict__ map, int Eg,
+                           int lo, int hi, int E, int32_t* next, int32_t* cnt,
+                           int32_t* __restrict__ sorted_ids, int32_t* __restrict__ slot_of) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
   for (int r0 = lo; r0 < hi; r0 += NWAVES * 64) {
     const int f = r0 + (int)threadIdx.x;
-    int e = -1;
-    if (f < hi) {
-      e = ids[f];
-      if (e < 0 || e >= E) e = -1;
-    }
+    const int e = f < hi ? local_expert(ids, f, map, Eg, E) : -1;
     const uint64_t peers = match_peers(e, key_bits(E));
     const int rank = __popcll(peers & below);
     const bool leader = e >= 0 && rank == 0;
@@ -154,7 +159,8 @@ __device__ void fill_padding(int32_t* routing, const int32_t* start, int E, int 
 // loaded once into registers for both the count and the placement.
 constexpr int kSmallRounds = kSmallMaxRows / 1024;
 
-__global__ __launch_bounds__(1024) void align_small(const int32_t* __restrict__ ids, int E, int B,
+__global__ __launch_bounds__(1024) void align_small(const int32_t* __restrict__ ids,
+                                                    const int32_t* __restrict__ map, int Eg, int E, int B,
                                                     int T, int topk, int cap, int nblocks,
                                                     int32_t* __restrict__ routing,
                                                     int64_t off_counts, int64_t off_offsets,
@@ -172,12 +178,7 @@ __global__ __launch_bounds__(1024) void align_small(const int32_t* __restrict__ 
 #pragma unroll
   for (int r = 0; r < kSmallRounds; ++r) {
     const int f = r * 1024 + (int)threadIdx.x;
-    int e = -1;
-    if (r < rounds && f < n) {
-      e = ids[f];
-      if (e < 0 || e >= E) e = -1;
-    }
-    my_e[r] = e;
+    my_e[r] = (r < rounds && f < n) ? local_expert(ids, f, map, Eg, E) : -1;
   }
   for (int i = threadIdx.x; i < 2 * (E + 1) + 16 * E; i += 1024) smem[i] = 0;
   __syncthreads();
@@ -228,6 +229,7 @@ __global__ __launch_bounds__(1024) void align_small(const int32_t* __restrict__ 
 
 // ---- large path ------------------------------------------------------------
 __global__ __launch_bounds__(kCountThreads) void align_count(const int32_t* __restrict__ ids,
+                                                             const int32_t* __restrict__ map, int Eg,
                                                              int n, int E,
                                                              int32_t* __restrict__ chunk_hist) {
   extern __shared__ int32_t hist[];
@@ -237,8 +239,8 @@ __global__ __launch_bounds__(kCountThreads) void align_count(const int32_t* __re
   for (int j = threadIdx.x; j < kAlignChunk; j += kCountThreads) {
     const int f = base + j;
     if (f < n) {
-      const int e = ids[f];
-      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+      const int e = local_expert(ids, f, map, Eg, E);
+      if (e >= 0) atomicAdd(&hist[e], 1);
     }
   }
   __syncthreads();
@@ -279,8 +281,9 @@ __global__ __launch_bounds__(kScanThreads) void align_scan(int32_t* __restrict__
 }
 
 template <int NWAVES>
-__global__ __launch_bounds__(NWAVES * 64) void align_scatter(const int32_t* __restrict__ ids, int n,
-                                                            int E, int32_t* __restrict__ routing,
+__global__ __launch_bounds__(NWAVES * 64) void align_scatter(const int32_t* __restrict__ ids,
+                                                            const int32_t* __restrict__ map, int Eg,
+                                                            int n, int E, int32_t* __restrict__ routing,
                                                             int64_t off_offsets, int64_t off_sorted,
                                                             int64_t off_slot_of, int64_t off_scratch) {
   extern __shared__ int32_t smem[];
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(NWAVES * 64) void align_scatter(const int32_t* __re
   for (int i = threadIdx.x; i < NWAVES * E; i += NWAVES * 64) cnt[i] = 0;
   __syncthreads();
   const int lo = chunk * kAlignChunk;
-  place_rows<NWAVES>(ids, lo, min(n, lo + kAlignChunk), E, next, cnt, routing + off_sorted,
+  place_rows<NWAVES>(ids, map, Eg, lo, min(n, lo + kAlignChunk), E, next, cnt, routing + off_sorted,
                      routing + off_slot_of);
 }
 
@@ -326,18 +329,20 @@ __global__ __launch_bounds__(256) void permute_rows(const uint16_t* __restrict__
 }  // namespace
 
 hipError_t launch_align(const int32_t* topk_ids, int T, int topk, int E, const RoutingLayout& L,
-                        int32_t* routing, hipStream_t s) {
+                        int32_t* routing, hipStream_t s, const int32_t* map, int Eg) {
   const int n = T * topk;
   if (n <= kSmallMaxRows && E <= kSmallMaxExperts) {
     const size_t lds = (size_t)(2 * (E + 1) + 16 * E) * sizeof(int32_t);
-    hipLaunchKernelGGL(align_small, dim3(1), dim3(1024), lds, s, topk_ids, E, L.block, T, topk, L.cap,
+    hipLaunchKernelGGL(align_small, dim3(1), dim3(1024), lds, s, topk_ids, map, Eg, E, L.block, T, topk,
+                       L.cap,
                        L.nblocks, routing, L.off_counts, L.off_offsets, L.off_sorted,
                        L.off_block_expert, L.off_slot_of);
     return hipGetLastError();
   }
   const size_t lds_e = (size_t)E * sizeof(int32_t);
   if (L.nchunks > 0) {
-    hipLaunchKernelGGL(align_count, dim3(L.nchunks), dim3(kCountThreads), lds_e, s, topk_ids, n, E,
+    hipLaunchKernelGGL(align_count, dim3(L.nchunks), dim3(kCountThreads), lds_e, s, topk_ids, map, Eg,
+                       n, E,
                        routing + L.off_scratch);
   }
   hipLaunchKernelGGL(align_scan, dim3(1), dim3(kScanThreads), lds_e + sizeof(int32_t), s, routing,
@@ -345,10 +350,12 @@ hipError_t launch_align(const int32_t* topk_ids, int T, int topk, int E, const R
                      L.off_sorted, L.off_block_expert, L.off_scratch);
   if (L.nchunks > 0) {
     if (E <= 2048)   // 4 waves per chunk: 5 E ints of LDS
-      hipLaunchKernelGGL(align_scatter<4>, dim3(L.nchunks), dim3(256), 5 * lds_e, s, topk_ids, n, E,
+      hipLaunchKernelGGL(align_scatter<4>, dim3(L.nchunks), dim3(256), 5 * lds_e, s, topk_ids, map, Eg,
+                         n, E,
                          routing, L.off_offsets, L.off_sorted, L.off_slot_of, L.off_scratch);
     else
-      hipLaunchKernelGGL(align_scatter<1>, dim3(L.nchunks), dim3(64), 2 * lds_e, s, topk_ids, n, E,
+      hipLaunchKernelGGL(align_scatter<1>, dim3(L.nchunks), dim3(64), 2 * lds_e, s, topk_ids, map, Eg,
+                         n, E,
                          routing, L.off_offsets, L.off_sorted, L.off_slot_of, L.off_scratch);
   }
   return hipGetLastError();

@@ -236,6 +236,7 @@ uint64_t key_of(int mode, int a, int b, const moe_tuning_t* o) {
     k = k * 1000003u + (uint32_t)o->block_m;
     k = k * 1000003u + (uint32_t)o->schedule;
     k = k * 1000003u + (uint32_t)o->dispatch;
+    k = k * 1000003u + (uint32_t)o->global_experts;
   }
   return k;
 }
@@ -265,7 +266,9 @@ Schedule schedule_indexed(moe_weights* h, int T, int topk, const moe_tuning_t* o
   auto it = h->cache.find(key);
   if (it != h->cache.end()) return it->second;
   Schedule s;
-  const int E = h->desc.num_experts;
+  // rows per expert: over the handle's experts, or with ovr.global_experts
+  // (expert parallelism) over the global pool the routing is drawn from
+  const int E = ovr && ovr->global_experts > 0 ? ovr->global_experts : h->desc.num_experts;
   const long rows = ((long)T * topk + E - 1) / E;
   s.rows = (int)rows;
   s.kind = rows < kLargeMRows ? SCHED_SMALL_M : SCHED_LARGE_M;
@@ -534,6 +537,10 @@ int32_t moe_routing_block(const moe_weights_t* h, int32_t T, int32_t topk, const
     fail(MOE_ERR_INVALID_ARG, "dispatch %d not in 0..2", ovr->dispatch);
     return 0;
   }
+  if (ovr && ovr->global_experts < 0) {
+    fail(MOE_ERR_INVALID_ARG, "global_experts %d < 0", ovr->global_experts);
+    return 0;
+  }
   if (large_m_rejected(h, ovr)) {
     fail(MOE_ERR_OVERRIDE_REJECTED,
          "large-M needs hidden and inter divisible by 128 and block_m 0 or 128 (got H=%d I=%d block_m=%d)",
@@ -573,9 +580,10 @@ size_t moe_routing_bytes(const moe_weights_t* h, int32_t T, int32_t topk, const 
   return (size_t)L.total_ints * 4;
 }
 
-moe_status_t moe_align(const moe_weights_t* h, const int32_t* topk_ids, int32_t T, int32_t topk,
-                       const moe_tuning_t* ovr, void* routing, size_t routing_bytes,
-                       moe_stream_t stream) {
+static moe_status_t align_impl(const moe_weights_t* h, const int32_t* topk_ids, int32_t T,
+                               int32_t topk, const int32_t* map, int32_t Eg,
+                               const moe_tuning_t* ovr, void* routing, size_t routing_bytes,
+                               moe_stream_t stream) {
   moe_status_t st = check_handle(h, MOE_MODE_INDEXED);
   if (st != MOE_OK) return st;
   if ((st = check_topk(h, T, topk)) != MOE_OK) return st;
@@ -592,10 +600,28 @@ moe_status_t moe_align(const moe_weights_t* h, const int32_t* topk_ids, int32_t 
   if ((st = set_device(h)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = run("align", s, [&] {
-    return launch_align(topk_ids, T, topk, h->desc.num_experts, R, (int32_t*)routing, s);
+    return launch_align(topk_ids, T, topk, h->desc.num_experts, R, (int32_t*)routing, s, map, Eg);
   });
   if (e != hipSuccess) return hip_fail(e, "align launch");
   return ok();
+}
+
+moe_status_t moe_align(const moe_weights_t* h, const int32_t* topk_ids, int32_t T, int32_t topk,
+                       const moe_tuning_t* ovr, void* routing, size_t routing_bytes,
+                       moe_stream_t stream) {
+  return align_impl(h, topk_ids, T, topk, nullptr, 0, ovr, routing, routing_bytes, stream);
+}
+
+moe_status_t moe_align_ep(const moe_weights_t* h, const int32_t* topk_ids, int32_t T, int32_t topk,
+                          const int32_t* expert_map, int32_t num_global_experts,
+                          const moe_tuning_t* ovr, void* routing, size_t routing_bytes,
+                          moe_stream_t stream) {
+  if (!expert_map || !aligned(expert_map, 4))
+    return fail(MOE_ERR_INVALID_ARG, "expert_map NULL or not 4-byte aligned");
+  if (num_global_experts < 1 || num_global_experts > (1 << 20))
+    return fail(MOE_ERR_INVALID_ARG, "num_global_experts %d outside 1..2^20", num_global_experts);
+  return align_impl(h, topk_ids, T, topk, expert_map, num_global_experts, ovr, routing,
+                    routing_bytes, stream);
 }
 
 moe_status_t moe_permute(const moe_weights_t* h, const uint16_t* x, int32_t T, int32_t topk,

@@ -75,8 +75,10 @@ hipError_t launch_gemm_large_m(const GemmParams& p, int set, int epi, hipStream_
 // multiple of 8; h rows of 2I, a rows of I, BF16).
 hipError_t launch_swiglu(const uint16_t* h, int64_t rows, int I, uint16_t* a, hipStream_t s);
 
+// map (NULL: ids are local): device int32 [Eg], global id -> local expert
+// of this handle or -1; rows whose id maps outside [0, E) are dropped.
 hipError_t launch_align(const int32_t* topk_ids, int T, int topk, int E, const RoutingLayout& L,
-                        int32_t* routing, hipStream_t s);
+                        int32_t* routing, hipStream_t s, const int32_t* map = nullptr, int Eg = 0);
 hipError_t launch_permute(const uint16_t* x, int T, int topk, int H, const RoutingLayout& L,
                           const int32_t* routing, uint16_t* a_out, int32_t* m_indices,
                           int32_t* row_src, hipStream_t s);
