@@ -50,9 +50,10 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="indexed workloads: time the unfused steps (align, gate_up GEMM with a BF16 "
                          "output, SwiGLU, down GEMM with a BF16 output; no combine) instead of the layer")
-    ap.add_argument("--dispatch", type=int, default=0, choices=(0, 1, 2),
-                    help="indexed small-M token-tile dispatch: 0 semi-static grid (default), "
-                         "1 persistent static ranges, 2 persistent atomic job queue")
+    ap.add_argument("--dispatch", type=int, default=0, choices=(0, 1, 2, 3),
+                    help="indexed small-M token-tile dispatch: 0 semi-static grid over experts "
+                         "(default), 1 persistent static ranges, 2 persistent atomic job queue, "
+                         "3 semi-static grid over routing blocks")
     ap.add_argument("--cpu-experts", type=int, default=48, help="experts in the oracle's timed sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (steps times), the "
@@ -310,7 +311,8 @@ def main():
         "config": {"workload": wl.name, "layout": wl.layout, "experts": wl.E, "hidden": wl.H,
                    "intermediate": wl.I, "tokens": wl.T, "topk": wl.topk, "rows": rows,
                    "experts_touched": touched, "weights": "uint4 g32 bf16-scale",
-                   "dispatch": ["semi-static", "persistent-static", "persistent-queue"][args.dispatch],
+                   "dispatch": ["semi-static", "persistent-static", "persistent-queue",
+                                "semi-static-blocks"][args.dispatch],
                    "steps": "unfused: align, gate_up, swiglu, down (BF16 hand-offs, no combine)"
                    if args.unfused else "fused layer",
                    "layer_packed_GBps": layer_packed / (ms * 1e-3) / 1e9,

@@ -100,13 +100,18 @@ typedef struct {
  *      equal contiguous range of (routing block, 256 weight rows) jobs;
  *   2  persistent, fully dynamic: the same workgroups taking jobs one at a
  *      time from an atomic counter in the workspace (cleared by the call with
- *      a fill kernel on its stream).
- * With 1 or 2 the routing block is one weight pass, 16 x the token tiles
- * (16, 32 or 64 rows), unless block_m sets it. */
+ *      a fill kernel on its stream);
+ *   3  semi-static over routing blocks: one workgroup per (routing block,
+ *      256 weight rows), the grid bounded by min(blocks, T*topk), so that a
+ *      call with few routed rows launches no workgroup per idle expert.
+ * With 1, 2 or 3 the routing block is one weight pass, 16 x the token tiles
+ * (16, 32 or 64 rows), unless block_m sets it. The semi-static forms (0, 3)
+ * may split K over several workgroups when the grid cannot fill the chip
+ * (FP32 partials in the workspace, summed in split order). */
 typedef struct {
   int32_t block_m;  /* alignment block (rows): 16, 32, 64 or 128 */
   int32_t schedule; /* 0 auto, 1 small-M (decode), 2 large-M (prefill) */
-  int32_t dispatch; /* small-M token-tile dispatch: 0, 1 or 2 (above) */
+  int32_t dispatch; /* small-M token-tile dispatch: 0 .. 3 (above) */
   int32_t global_experts; /* expert parallelism: experts the routing is drawn
                              from (0: the handle's); rows per expert, which pick
                              the schedule, are T*topk / global_experts */

@@ -78,6 +78,10 @@ WORKLOADS = {
     6: Workload("kimi-ep8-share-prefill-contiguous-e48-h7168-i2048-512rows-per-expert", "contiguous",
                 E=48, H=7168, I=2048, T=0, topk=0, routing="none",
                 wseed=101, iseed=206, extra={"rows_per_expert": 512}),
+    # batch-1 decode: 8 experts touched, the latency case
+    7: Workload("kimi-decode-indexed-e384-h7168-i2048-t1-top8", "indexed",
+                E=384, H=7168, I=2048, T=1, topk=8, routing="softmax",
+                wseed=101, iseed=207),
 }
 
 

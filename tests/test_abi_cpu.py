@@ -235,7 +235,8 @@ def test_schedule_choice_by_rows_per_expert(L):
     assert L.moe_routing_block(p.h, 100, 4, ctypes.byref(M.Tuning(0, 0, 1, 0))) == 32
     assert L.moe_routing_block(p.h, 40, 4, ctypes.byref(M.Tuning(0, 0, 2, 0))) == 16
     assert L.moe_routing_block(p.h, 320, 4, ctypes.byref(M.Tuning(0, 0, 2, 0))) == 128   # large-M
-    assert L.moe_routing_block(p.h, 100, 4, ctypes.byref(M.Tuning(0, 0, 3, 0))) == 0
+    assert L.moe_routing_block(p.h, 100, 4, ctypes.byref(M.Tuning(0, 0, 3, 0))) == 32
+    assert L.moe_routing_block(p.h, 100, 4, ctypes.byref(M.Tuning(0, 0, 4, 0))) == 0
     assert "dispatch" in M.last_error()
     tail = Plan(L, "indexed", E=16, H=160, I=96)               # K not whole 128-chunks
     assert L.moe_routing_block(tail.h, 320, 4, None) == 16

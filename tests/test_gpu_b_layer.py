@@ -208,12 +208,13 @@ DISPATCH_CASES = [
 ]
 
 
-@pytest.mark.parametrize("dispatch", [1, 2])
+@pytest.mark.parametrize("dispatch", [1, 2, 3])
 @pytest.mark.parametrize("E,H,I,T,topk,wgs", DISPATCH_CASES)
 def test_indexed_small_dispatch(E, H, I, T, topk, wgs, dispatch, monkeypatch):
-    """Persistent static and job-queue dispatch against the oracle: outputs
-    and the intermediate a, with the weight and token streams running on
-    across job boundaries."""
+    """Persistent static and job-queue dispatch, and the semi-static grid over
+    routing blocks, against the oracle: outputs and the intermediate a, with
+    the persistent forms' weight and token streams running on across job
+    boundaries."""
     require_gpu()
     import torch
     log(f"case dispatch={dispatch} E={E} H={H} I={I} T={T} topk={topk} wgs={wgs}")
@@ -228,7 +229,7 @@ def test_indexed_small_dispatch(E, H, I, T, topk, wgs, dispatch, monkeypatch):
     h = prepare(w, "indexed")
     d = h.describe(T, topk, ovr=ovr)
     log(f"  {d}")
-    assert "small-M" in d and "dispatch=persistent" in d
+    assert "small-M" in d and ("dispatch=persistent" in d if dispatch < 3 else "semi-static-blocks" in d)
     ids_d = i32_dev(ids)
     routing = h.align(ids_d, ovr=ovr)
     ws = torch.empty(h.workspace_bytes(T, topk, T, ovr=ovr), dtype=torch.uint8, device="cuda")
@@ -253,6 +254,7 @@ def test_indexed_small_dispatch(E, H, I, T, topk, wgs, dispatch, monkeypatch):
     (64, 8, 256, 128, 200, 8, "contiguous"),     # decode-like share: ~25 local rows per expert
     (64, 8, 256, 128, 200, 8, "round-robin"),
     (32, 4, 256, 256, 640, 4, "contiguous"),     # prefill-like share: ~80 rows per expert (large-M)
+    (64, 8, 256, 128, 1, 4, "round-robin"),      # one token: fewer rows than local experts
 ])
 def test_indexed_ep_share(Eg, E, H, I, T, topk, placement):
     """The layer on one GPU's expert share: only local rows are summed, tokens
@@ -275,3 +277,53 @@ def test_indexed_ep_share(Eg, E, H, I, T, topk, placement):
     none = np.all(loc < 0, axis=1)
     assert np.all(out[none] == 0)
     check_tol(out, ref, "indexed EP share")
+
+
+SPLIT_CASES = [
+    # (E, H, I, T, topk, forced split or 0 for the automatic choice, ovr):
+    # grid-starved small-M calls split K over several workgroups and reduce
+    # the partials (in split order) in the SwiGLU and in the combine
+    (32, 2048, 1024, 1, 8, 0, None),        # one token: W13 split 2 (8 chunks each)
+    (32, 2048, 1024, 3, 8, 0, None),
+    (16, 384, 256, 40, 4, 2, None),         # forced: 3 chunks over 2 splits (uneven)
+    (16, 160, 96, 37, 4, 2, None),          # forced: K tails, 2 chunks over 2 splits
+    (16, 256, 128, 40, 4, 3, None),         # forced beyond the chunk count: capped
+    (64, 1024, 512, 60, 8, 0, {"global_experts": 512}),   # an EP share's schedule
+    (32, 2048, 1024, 1, 8, 1, None),        # forced 1: the active-expert grid (8 sets of 32) alone
+    (32, 2048, 1024, 1, 8, 0, {"dispatch": 3}),           # over routing blocks
+    (16, 384, 256, 40, 4, 2, {"dispatch": 3}),
+]
+
+
+@pytest.mark.parametrize("E,H,I,T,topk,split,ovr", SPLIT_CASES)
+def test_indexed_small_split_k(E, H, I, T, topk, split, ovr, monkeypatch):
+    require_gpu()
+    import torch
+    log(f"case split-K E={E} H={H} I={I} T={T} topk={topk} split={split} ovr={ovr}")
+    if split:
+        monkeypatch.setenv("MOE_W4A16_KSPLIT", str(split))
+    w = tiny_weights(E, H, I, seed=E * 7 + H)
+    x = synth.activations(61, T, H)
+    ids, tw = synth.softmax_routing(62, T, E, topk)
+    h = prepare(w, "indexed")
+    d = h.describe(T, topk, ovr=ovr)
+    log(f"  {d}")
+    assert "small-M" in d
+    if not split and not (ovr or {}).get("global_experts"):
+        assert "ksplit=1/1" not in d
+    ids_d = i32_dev(ids)
+    routing = h.align(ids_d, ovr=ovr)
+    ws = torch.empty(h.workspace_bytes(T, topk, T, ovr=ovr), dtype=torch.uint8, device="cuda")
+    out = h.indexed(bf16_dev(x), ids_d, f32_dev(tw), routing=routing, ws=ws, ovr=ovr)
+    torch.cuda.synchronize()
+    ref, inter = O.moe_indexed(x, ids, tw, w, E=E, keep=True)
+    check_tol(O.bf16_to_f64(bits_host(out)), ref, "indexed split-K")
+    lay = h.routing_layout(T, topk, ovr)
+    sid = routing.cpu().numpy()[lay.off_sorted:lay.off_sorted + lay.cap]
+    a_ws = ws[: lay.cap * I * 2].view(torch.int16).view(lay.cap, I).cpu().numpy().view(np.uint16)
+    slots = np.flatnonzero(sid < T * topk)
+    ref_a = np.stack([inter["a"][int(f)] for f in sid[slots]])
+    frac, mx, within = a_mismatch(a_ws[slots], ref_a, "indexed split-K")
+    assert within and frac < 1e-3
+    out2 = h.indexed(bf16_dev(x), ids_d, f32_dev(tw), routing=routing, ws=ws, ovr=ovr)
+    assert np.array_equal(bits_host(out2), bits_host(out)), "split-K result depends on the run"

@@ -61,6 +61,7 @@ struct EnvOverrides {
   int log = 0;        // MOE_W4A16_LOG: print each new schedule
   int no_resident = 0;   // MOE_W4A16_NO_RESIDENT: keep the K-loop form of large-M for short K
   int job_wgs = 0;       // MOE_W4A16_JOB_WGS: cap on the persistent small-M grid (tests: long job walks)
+  int ksplit = 0;        // MOE_W4A16_KSPLIT: force the small-M split-K factor (tests)
   void read() {
     auto geti = [](const char* k) {
       const char* v = std::getenv(k);
@@ -71,6 +72,7 @@ struct EnvOverrides {
     log = geti("MOE_W4A16_LOG");
     no_resident = geti("MOE_W4A16_NO_RESIDENT");
     job_wgs = geti("MOE_W4A16_JOB_WGS");
+    ksplit = geti("MOE_W4A16_KSPLIT");
   }
 };
 
@@ -160,7 +162,9 @@ struct Schedule {
   int kind = SCHED_SMALL_M;
   int block = 16;   // routing alignment block (indexed)
   int nt = 1;       // 16-row token tiles per weight pass (small-M)
-  int dispatch = 0; // small-M: 0 semi-static grid, 1 persistent static ranges, 2 persistent job queue
+  int dispatch = 0; // small-M: 0 semi-static grid over experts, 1 persistent static ranges,
+                    // 2 persistent job queue, 3 semi-static grid over routing blocks
+  int ksplit13 = 1, ksplit2 = 1;   // small-M semi-static: K splits of W13 / W2 (grid-starved calls)
   int rows = 0;     // rows per expert the choice was made for
 };
 
@@ -205,6 +209,20 @@ hipError_t run_gemm(int mat, const Schedule& sc, const GemmParams& p0, int set, 
   if (p.dispatch) p.total_wg = job_grid(p.nsets, p.passes, p.wg_per_set, sc.nt, env);
   return run(mat == 13 ? "gemm_w13_small_m" : "gemm_w2_small_m", s,
              [&] { return launch_gemm_small_m(p, set, epi, sc.nt, s); });
+}
+
+// Routing blocks that can hold rows: each holds at least one of the T*topk.
+int block_bound(const RoutingLayout& R, int T, int topk) {
+  const int64_t flat = (int64_t)T * topk;
+  return flat < R.nblocks ? (int)flat : R.nblocks;
+}
+
+// Experts that can hold rows: the per-expert small-M grid covers this many
+// sets, the kernel mapping set i to the i-th expert with rows when it is
+// below E.
+int expert_bound(int E, int T, int topk) {
+  const int64_t flat = (int64_t)T * topk;
+  return flat < E ? (int)flat : E;
 }
 
 int nt_for_rows(int rows) {
@@ -279,9 +297,31 @@ Schedule schedule_indexed(moe_weights* h, int T, int topk, const moe_tuning_t* o
   s.nt = nt_for_rows((int)rows);
   if (h->env.nt) s.nt = h->env.nt;
   if (ovr && s.kind == SCHED_SMALL_M) s.dispatch = ovr->dispatch;
-  // the persistent forms take one routing block per weight pass of 16*nt rows
+  // the routing-block forms take one block per weight pass of 16*nt rows
   s.block = s.kind == SCHED_LARGE_M ? 128 : (s.dispatch ? 16 * s.nt : 16);
   if (ovr && ovr->block_m) s.block = ovr->block_m;
+  if (s.kind == SCHED_SMALL_M && (s.dispatch == 0 || s.dispatch == 3)) {
+    // split K when the grid cannot fill the resident slots: at most
+    // min(E, local rows) experts hold rows, each with ceil(RG/4) quads
+    const int Eh = h->desc.num_experts;
+    const long flat = (long)T * topk;
+    const long local = ovr && ovr->global_experts > 0 ? (flat * Eh + ovr->global_experts - 1) / ovr->global_experts
+                                                      : flat;
+    const long sets = local < Eh ? local : Eh;
+    const int slots = 256 * (s.nt == 1 ? 4 : (s.nt == 2 ? 3 : 2));
+    auto split_for = [&](const MatLayout& m) {
+      const long wgs = sets * ((m.RG + 3) / 4);
+      int k = 1;
+      if (wgs > 0 && 2 * wgs <= slots) k = (int)((slots + wgs - 1) / wgs);   // under half full
+      if (h->env.ksplit > 0) k = h->env.ksplit;
+      const int kmax = m.Kc / 8 > 1 ? m.Kc / 8 : 1;   // at least 8 chunks per split
+      if (k > 8) k = 8;
+      if (k > kmax) k = h->env.ksplit > 0 ? (h->env.ksplit < m.Kc ? h->env.ksplit : m.Kc) : kmax;
+      return k < 1 ? 1 : k;
+    };
+    s.ksplit13 = split_for(h->lay.w13);
+    s.ksplit2 = split_for(h->lay.w2);
+  }
   if (h->env.log)
     std::fprintf(stderr, "[moe_w4a16] indexed T=%d topk=%d rows/expert=%ld -> %s nt=%d block=%d\n",
                  T, topk, rows, kind_name(s.kind), s.nt, s.block);
@@ -372,10 +412,10 @@ moe_status_t check_topk(const moe_weights_t* h, int T, int topk) {
 // the second GEMM (one per flat routed row, summed by the combine), the
 // contiguous layout's row-validity map, and the indexed layout's own routing.
 struct WsLayout {
-  size_t off_a = 0, off_y = 0, off_queue = 0, off_valid = 0, off_routing = 0, total = 0;
+  size_t off_a = 0, off_y = 0, off_part = 0, off_queue = 0, off_valid = 0, off_routing = 0, total = 0;
 };
 
-WsLayout ws_indexed(const moe_weights_t* h, int T, int topk, int block) {
+WsLayout ws_indexed(const moe_weights_t* h, int T, int topk, int block, const Schedule& sc) {
   RoutingLayout R;
   R.init(h->desc.num_experts, T, topk, block);
   WsLayout w;
@@ -384,6 +424,11 @@ WsLayout ws_indexed(const moe_weights_t* h, int T, int topk, int block) {
   o = round_up(o + (size_t)R.cap * h->desc.inter * 2, kAlign);
   w.off_y = o;
   o = round_up(o + (size_t)T * topk * h->desc.hidden * 4, kAlign);
+  // split-K partials: [ksplit][T*topk][N] FP32 per GEMM (one at a time)
+  w.off_part = o;
+  const size_t p13 = sc.ksplit13 > 1 ? (size_t)sc.ksplit13 * 2 * h->desc.inter : 0;
+  const size_t p2 = sc.ksplit2 > 1 ? (size_t)sc.ksplit2 * h->desc.hidden : 0;
+  o = round_up(o + (size_t)T * topk * (p13 > p2 ? p13 : p2) * 4, kAlign);
   w.off_queue = o;   // job counters of the persistent small-M dispatch (W13, W2)
   o += kAlign;
   w.off_valid = w.off_routing = o;
@@ -533,8 +578,8 @@ int32_t moe_routing_block(const moe_weights_t* h, int32_t T, int32_t topk, const
     fail(MOE_ERR_INVALID_ARG, "block_m %d not in {16, 32, 64, 128}", ovr->block_m);
     return 0;
   }
-  if (ovr && (ovr->dispatch < 0 || ovr->dispatch > 2)) {
-    fail(MOE_ERR_INVALID_ARG, "dispatch %d not in 0..2", ovr->dispatch);
+  if (ovr && (ovr->dispatch < 0 || ovr->dispatch > 3)) {
+    fail(MOE_ERR_INVALID_ARG, "dispatch %d not in 0..3", ovr->dispatch);
     return 0;
   }
   if (ovr && ovr->global_experts < 0) {
@@ -654,7 +699,8 @@ size_t moe_workspace_bytes(const moe_weights_t* h, int32_t mode, int32_t rows, i
   if (mode == MOE_MODE_INDEXED) {
     const int B = moe_routing_block(h, rows, topk, ovr);
     if (!B) return 0;
-    return ws_indexed(h, rows, topk, B).total;
+    return ws_indexed(h, rows, topk, B, schedule_indexed(const_cast<moe_weights_t*>(h), rows, topk, ovr))
+        .total;
   }
   if (rows < 0 || tokens < 0) {
     fail(MOE_ERR_INVALID_ARG, "negative rows / tokens");
@@ -684,7 +730,7 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
       (routing && !aligned(routing, 4)) || (topk_ids && !aligned(topk_ids, 4)))
     return fail(MOE_ERR_INVALID_ARG, "misaligned pointer (x/out 16 B, ws 256 B, others 4 B)");
   const Schedule sc = schedule_indexed(h, T, topk, ovr);
-  const WsLayout W = ws_indexed(h, T, topk, B);
+  const WsLayout W = ws_indexed(h, T, topk, B, sc);
   const size_t need = routing ? W.off_routing : W.total;
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu", ws_bytes, need);
@@ -713,13 +759,13 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   p.topk = topk;
   p.block = B;
   p.block_expert = rt + R.off_block_expert;
-  // semi-static small-M: one row set per expert; large-M and the persistent
-  // small-M forms: one per routing block
+  // semi-static small-M over experts: one row set per expert; large-M and
+  // the other small-M forms: one per routing block
   const bool large = sc.kind == SCHED_LARGE_M;
   const bool blocks = large || sc.dispatch;
-  p.nsets = blocks ? R.nblocks : E;
+  p.nsets = blocks ? block_bound(R, T, topk) : expert_bound(E, T, topk);
   const int set = blocks ? SET_ROUTED : SET_INDEXED;
-  if (!large && sc.dispatch) {
+  if (!large && (sc.dispatch == 1 || sc.dispatch == 2)) {
     p.dispatch = sc.dispatch;
     p.passes = (B + 16 * sc.nt - 1) / (16 * sc.nt);
   }
@@ -736,8 +782,22 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   p13.gather = 1;
   p13.a_out = a_ws;
   p13.a_ld = I;
+  float* part = (float*)(wsb + W.off_part);
+  const int64_t F = (int64_t)T * topk;
+  const bool semi = !large && (sc.dispatch == 0 || sc.dispatch == 3);
+  const bool split13 = semi && sc.ksplit13 > 1, split2 = semi && sc.ksplit2 > 1;
+  if (split13) {   // grid-starved: K split over ksplit13 workgroups, reduced with the SwiGLU
+    p13.ksplit = sc.ksplit13;
+    p13.total_wg *= sc.ksplit13;
+    p13.part = part;
+    p13.part_rows = F;
+  }
   if (e == hipSuccess)
-    e = run_gemm(13, sc, p13, set, EPI_SWIGLU, s, h->env);
+    e = run_gemm(13, sc, p13, set, split13 ? EPI_PARTIAL : EPI_SWIGLU, s, h->env);
+  if (e == hipSuccess && split13)
+    e = run("splitk_swiglu", s, [&] {
+      return launch_splitk_swiglu(part, sc.ksplit13, F, I, rt + R.off_sorted, R.cap, T * topk, a_ws, I, s);
+    });
 
   GemmParams p2 = p;
   fill_weights(p2, h, h->lay.w2);
@@ -748,11 +808,19 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   p2.yrows = yrows;
   p2.topk_w = topk_w;
   p2.yrows_ld = H;
+  if (split2) {   // reduced by the combine
+    p2.ksplit = sc.ksplit2;
+    p2.total_wg *= sc.ksplit2;
+    p2.part = part;
+    p2.part_rows = F;
+  }
   if (e == hipSuccess)
-    e = run_gemm(2, sc, p2, set, EPI_COMBINE, s, h->env);
+    e = run_gemm(2, sc, p2, set, split2 ? EPI_PARTIAL : EPI_COMBINE, s, h->env);
   if (e == hipSuccess)
     e = run("combine_topk", s, [&] {
-      return launch_combine_rows(yrows, rt + R.off_slot_of, rt, E, B, T, topk, H, out, s);
+      return split2 ? launch_splitk_combine(part, sc.ksplit2, rt + R.off_slot_of, rt, E, B, topk_w, T, topk,
+                                            H, out, s)
+                    : launch_combine_rows(yrows, rt + R.off_slot_of, rt, E, B, T, topk, H, out, s);
     });
   if (e != hipSuccess) return hip_fail(e, "indexed launch");
   return ok();
@@ -792,7 +860,7 @@ static moe_status_t indexed_gemm_step(const moe_weights_t* hc, int mat, const ui
   p.block = B;
   p.block_expert = rt + R.off_block_expert;
   const bool large = sc.kind == SCHED_LARGE_M;
-  p.nsets = large ? R.nblocks : E;
+  p.nsets = large ? block_bound(R, T, topk) : expert_bound(E, T, topk);
   const int set = large ? SET_ROUTED : SET_INDEXED;
   fill_weights(p, h, mat == 13 ? h->lay.w13 : h->lay.w2);
   p.total_wg = p.nsets * p.wg_per_set;
@@ -1000,17 +1068,20 @@ int moe_describe(const moe_weights_t* hc, int32_t mode, int32_t rows, int32_t to
     const Schedule s = schedule_indexed(h, rows, topk, ovr);
     RoutingLayout R;
     R.init(E, rows, topk, s.block);
-    const bool persistent = s.kind == SCHED_SMALL_M && s.dispatch;
-    const int sets = s.kind == SCHED_LARGE_M || persistent ? R.nblocks : E;
+    const bool persistent = s.kind == SCHED_SMALL_M && (s.dispatch == 1 || s.dispatch == 2);
+    const int sets = s.kind == SCHED_LARGE_M || s.dispatch ? block_bound(R, rows, topk)
+                                                           : expert_bound(E, rows, topk);
     const int P = (s.block + 16 * s.nt - 1) / (16 * s.nt);
     const int g13 = persistent ? job_grid(sets, P, wg13, s.nt, h->env) : sets * wg13;
     const int g2 = persistent ? job_grid(sets, P, wg2, s.nt, h->env) : sets * wg2;
-    static const char* kDispatch[] = {"semi-static", "persistent-static", "persistent-queue"};
+    static const char* kDispatch[] = {"semi-static", "persistent-static", "persistent-queue",
+                                      "semi-static-blocks"};
     len = std::snprintf(buf, n,
                         "layout=indexed T=%d topk=%d rows_per_expert=%d schedule=%s block=%d nt=%d "
-                        "grid_w13=%d grid_w2=%d dispatch=%s",
-                        rows, topk, s.rows, kind_name(s.kind), s.block, s.nt, g13, g2,
-                        s.kind == SCHED_SMALL_M ? kDispatch[s.dispatch] : "routing-blocks");
+                        "grid_w13=%d grid_w2=%d dispatch=%s ksplit=%d/%d",
+                        rows, topk, s.rows, kind_name(s.kind), s.block, s.nt, g13 * s.ksplit13,
+                        g2 * s.ksplit2, s.kind == SCHED_SMALL_M ? kDispatch[s.dispatch] : "routing-blocks",
+                        s.ksplit13, s.ksplit2);
   } else if (mode == MOE_MODE_MASKED) {
     if (expected_m <= 0 || rows < 0) return -1;
     const Schedule s = schedule_masked(h, rows, expected_m);

@@ -20,6 +20,16 @@ namespace {
 // contiguous layout's rows). With a routing header that does not describe
 // (E, block, T*topk) nothing was computed and the result is zero, as for the
 // GEMMs.
+// y where v, else +0 in every lane, by a mask rather than a select, so that
+// the load feeding it is not moved under a branch.
+__device__ __forceinline__ f32x4_t keep_if(f32x4_t y, bool v) {
+  const uint32_t m = v ? ~0u : 0u;
+  f32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __uint_as_float(__float_as_uint(y[i]) & m);
+  return r;
+}
+
 __global__ __launch_bounds__(256) void combine_rows(const f32x4_t* __restrict__ yrows,
                                                     const int32_t* __restrict__ valid,
                                                     const int32_t* __restrict__ hdr, int E, int block,
@@ -32,9 +42,80 @@ __global__ __launch_bounds__(256) void combine_rows(const f32x4_t* __restrict__ 
                            hdr[HDR_E] == E && hdr[HDR_T] * hdr[HDR_TOPK] == T * topk);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   if (ok) {
+    // one row at a time: with a token per workgroup row the grid has the
+    // parallelism, and skipped rows (another GPU's experts) cost no reads
     for (int j = 0; j < topk; ++j) {
       const int f = t * topk + j;
       if (valid[f] >= 0) acc += __builtin_nontemporal_load(yrows + (size_t)f * H4 + c);
+    }
+  }
+  u32x2_t r;
+  r[0] = pack_bf16x2(acc[0], acc[1]);
+  r[1] = pack_bf16x2(acc[2], acc[3]);
+  out[(size_t)t * H4 + c] = r;
+}
+
+// Split-K reduction of W13 fused with its SwiGLU: one thread per (routing
+// slot, 4 consecutive output columns). Output column c is gate row
+// rg*64 + 2*pp*16 + r and up row rg*64 + (2*pp + 1)*16 + r of the prepared
+// (interleaved) order, rg = c / 32, pp = (c / 16) % 2, r = c % 16; four
+// consecutive columns are four consecutive prepared rows. Partials add in
+// split order, so the result does not depend on scheduling.
+__global__ __launch_bounds__(256) void splitk_swiglu(const float* __restrict__ part, int S, int64_t F,
+                                                     int I, const int32_t* __restrict__ sorted_ids,
+                                                     int cap, int sentinel, uint16_t* __restrict__ a,
+                                                     int64_t a_ld) {
+  const int I4 = I / 4;
+  const int64_t n = (int64_t)cap * I4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int slot = (int)(i / I4);
+    const int c = (int)(i - (int64_t)slot * I4) * 4;
+    const int f = sorted_ids[slot];
+    if (f < 0 || f >= sentinel) continue;
+    const int rg = c >> 5, pp = (c >> 4) & 1, r = c & 15;
+    const int gr = rg * 64 + 2 * pp * 16 + r, ur = gr + 16;
+    f32x4_t g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < S; ++ks) {
+      const float* row = part + ((size_t)ks * F + f) * (2 * I);
+      g += *reinterpret_cast<const f32x4_t*>(row + gr);
+      u += *reinterpret_cast<const f32x4_t*>(row + ur);
+    }
+    u32x2_t v;
+    v[0] = pack_bf16x2(swiglu(g[0], u[0]), swiglu(g[1], u[1]));
+    v[1] = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
+    *reinterpret_cast<u32x2_t*>(a + (size_t)slot * a_ld + c) = v;
+  }
+}
+
+// Split-K reduction of W2 fused with the combine: one thread per (token, 4
+// features); out[t] = bf16(sum over j ascending of w[t,j] * y(t,j)) with
+// y = the split partials added in split order, rows with slot_of < 0 left
+// out, as combine_rows does for the unsplit rows.
+__global__ __launch_bounds__(256) void splitk_combine(const float* __restrict__ part, int S,
+                                                      const int32_t* __restrict__ slot_of,
+                                                      const int32_t* __restrict__ hdr, int E, int block,
+                                                      const float* __restrict__ topk_w, int T, int topk,
+                                                      int H4, u32x2_t* __restrict__ out) {
+  const int t = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T || c >= H4) return;
+  const bool ok = hdr[HDR_MAGIC] == kRoutingMagic && hdr[HDR_BLOCK] == block && hdr[HDR_E] == E &&
+                  hdr[HDR_T] * hdr[HDR_TOPK] == T * topk;
+  const int64_t F = (int64_t)T * topk;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (ok) {
+    const int64_t f0 = (int64_t)t * topk;
+    for (int j = 0; j < topk; ++j) {
+      // loads without a branch (split calls are grid-starved: latency, not
+      // bandwidth, decides), an invalid row's reads repeating the token's
+      // first row and adding bitwise zeros
+      const bool v = slot_of[f0 + j] >= 0;
+      const int64_t f = f0 + (v ? j : 0);
+      f32x4_t y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int ks = 0; ks < S; ++ks)
+        y += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(part) + ((size_t)ks * F + f) * H4 + c);
+      acc += topk_w[f] * keep_if(y, v);
     }
   }
   u32x2_t r;
@@ -95,6 +176,28 @@ hipError_t launch_swiglu(const uint16_t* h, int64_t rows, int I, uint16_t* a, hi
   const int64_t blocks = (n + 255) / 256;
   hipLaunchKernelGGL(swiglu_rows, dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(256), 0, s,
                      reinterpret_cast<const u32x4_t*>(h), rows, I / 8, reinterpret_cast<u32x4_t*>(a));
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_swiglu(const float* part, int S, int64_t F, int I, const int32_t* sorted_ids,
+                                int cap, int sentinel, uint16_t* a, int64_t a_ld, hipStream_t s) {
+  if (cap <= 0) return hipSuccess;
+  if (I % 32 || S < 1) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)cap * (I / 4);
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(splitk_swiglu, dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(256), 0, s,
+                     part, S, F, I, sorted_ids, cap, sentinel, a, a_ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_combine(const float* part, int S, const int32_t* slot_of, const int32_t* hdr,
+                                 int E, int block, const float* topk_w, int T, int topk, int H,
+                                 uint16_t* out, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (H % 4 || S < 1 || !hdr) return hipErrorInvalidValue;
+  const int H4 = H / 4;
+  hipLaunchKernelGGL(splitk_combine, dim3((H4 + 255) / 256, T), dim3(256), 0, s, part, S, slot_of, hdr, E,
+                     block, topk_w, T, topk, H4, reinterpret_cast<u32x2_t*>(out));
   return hipGetLastError();
 }
 

@@ -146,6 +146,24 @@ __device__ __forceinline__ int wave_max(int v) {
   return v;
 }
 
+// The n-th expert (in expert order) with rows in counts[0, E), or -1: one
+// ballot per 64 experts, the same answer in every lane of the wave.
+__device__ __forceinline__ int nth_active(const int32_t* counts, int E, int n) {
+  const int lane = threadIdx.x & 63;
+  for (int base = 0; base < E; base += 64) {
+    const bool has = base + lane < E && counts[base + lane] > 0;
+    const uint64_t m = __ballot(has);
+    const int k = __popcll(m);
+    if (n < k) {
+      const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+      const uint64_t hit = __ballot(has && __popcll(m & below) == n);
+      return base + __builtin_ctzll(hit);
+    }
+    n -= k;
+  }
+  return -1;
+}
+
 // Output column of a BF16 store epilogue for lane `lane` of MFMA tile mt of
 // row group rg (4 columns from the returned one), or -1 past the output.
 // A W13 store (gate_up_I = I) undoes the prepared gate/up interleave: tiles

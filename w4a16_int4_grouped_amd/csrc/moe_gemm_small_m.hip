@@ -156,11 +156,14 @@ constexpr int kSmallMBlocksPerCU = NT == 1 ? 4 : (NT == 2 ? 3 : 2);
 template <int NT, int SET, int EPI>
 __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(const GemmParams p) {
   // rows of x gathered through the routing (W13 of the indexed layout)
-  const bool gather = SET == SET_INDEXED && p.gather;
+  const bool gather = (SET == SET_INDEXED || SET == SET_ROUTED) && p.gather;
   __shared__ TileLds<NT> lds;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-  const int logical = xcd_remap(blockIdx.x, p.total_wg);
+  const int logical_k = xcd_remap(blockIdx.x, p.total_wg);
+  // split K: ksplit consecutive workgroups share one (set, quad)
+  const int S = p.ksplit > 1 ? p.ksplit : 1;
+  const int ks = logical_k % S, logical = logical_k / S;
   const int set = logical / p.wg_per_set;
   const int rg_raw = (logical - set * p.wg_per_set) * 4 + wave;
   const bool active = rg_raw < p.RG;          // waves past the last row group still load tiles
@@ -173,9 +176,24 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
     if (hdr[HDR_MAGIC] != kRoutingMagic || hdr[HDR_BLOCK] != p.block || hdr[HDR_E] != p.E ||
         hdr[HDR_T] * hdr[HDR_TOPK] != p.sentinel)
       return;   // routing made for other shapes: compute nothing
-    e = set;
+    // a grid of fewer sets than experts (fewer routed rows than experts)
+    // takes the experts that hold rows, in expert order
+    e = p.nsets < p.E ? nth_active(p.counts, p.E, set) : set;
+    if (e < 0) return;
     slot0 = p.offsets[e];
     count = p.counts[e];
+  } else if constexpr (SET == SET_ROUTED) {
+    // one routing block of p.block slots; the grid covers a host bound on the
+    // blocks, the header's total says which hold rows
+    const int32_t* hdr = p.routing_hdr;
+    if (hdr[HDR_MAGIC] != kRoutingMagic || hdr[HDR_BLOCK] != p.block || hdr[HDR_E] != p.E ||
+        hdr[HDR_T] * hdr[HDR_TOPK] != p.sentinel)
+      return;
+    if (set >= min(max(hdr[HDR_TOTAL], 0) / p.block, p.nsets)) return;
+    e = p.block_expert[set];
+    if (e >= p.E) return;
+    slot0 = set * p.block;
+    count = p.block;   // pad slots hold the sentinel: read row 0, never written
   } else if constexpr (SET == SET_MASKED) {
     e = set;
     slot0 = e * p.max_m;
@@ -192,18 +210,20 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
   }
   if (count <= 0 || e < 0) return;
 
-  const size_t tile0 = ((size_t)e * p.RG + rg) * p.Kc;
+  // this workgroup's chunks c0 .. c0 + Kc of the row group's p.Kc
+  const int c0 = (int)((int64_t)p.Kc * ks / S);
+  const int Kc = (int)((int64_t)p.Kc * (ks + 1) / S) - c0;
+  const size_t tile0 = ((size_t)e * p.RG + rg) * p.Kc + c0;
   const size_t cstride = 1;   // tiles between consecutive chunks of a row group
   const u32x4_t* __restrict__ wq = reinterpret_cast<const u32x4_t*>(p.wq) + tile0 * (kMT * 64);
   const u32x2_t* __restrict__ ws = reinterpret_cast<const u32x2_t*>(p.wsc) + tile0 * 64;
   // dummy source for prefetches past the last chunk (valid, quickly cached)
   const u32x4_t* __restrict__ wq_dummy = reinterpret_cast<const u32x4_t*>(p.wq);
   const u32x2_t* __restrict__ ws_dummy = reinterpret_cast<const u32x2_t*>(p.wsc);
-  const int Kc = p.Kc;
   const uint32_t mlo = kF16MagicLo, mhi = kF16MagicHi;
   const int lr = threadIdx.x >> 4;             // token row this thread loads into LDS
   const int lpiece = (threadIdx.x & 15) * 8;   // its k offset within a chunk
-  const int kmax = p.K - lpiece;               // chunk kc is readable if kc*128 < kmax
+  const int kmax = p.K - c0 * kKC - lpiece;    // local chunk kc is readable if kc*128 < kmax
 
   for (int tb = 0; tb < count; tb += 16 * NT) {
     const uint16_t* lrow[NT];
@@ -211,8 +231,12 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
     for (int nt = 0; nt < NT; ++nt) {
       const int r = min(tb + nt * 16 + lr, count - 1);   // pad columns repeat a valid row
       const int slot = slot0 + r;
-      const int row = gather ? p.sorted_ids[slot] / p.topk : slot;
-      lrow[nt] = p.src + (size_t)row * p.src_ld + lpiece;
+      int row = slot;
+      if (gather) {
+        const int f = p.sorted_ids[slot];
+        row = (f >= 0 && f < p.sentinel) ? f / p.topk : 0;   // pad slots read row 0
+      }
+      lrow[nt] = p.src + (size_t)row * p.src_ld + c0 * kKC + lpiece;
     }
     f32x4_t acc[kMT][NT];
 #pragma unroll
@@ -261,6 +285,10 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
       const int r = tb + nt * 16 + (lane & 15);
       if (r >= count) continue;
       const int slot = slot0 + r;
+      if constexpr (SET == SET_ROUTED) {
+        const int f = p.sorted_ids[slot];
+        if (f < 0 || f >= p.sentinel) continue;   // pad slot
+      }
       if constexpr (EPI == EPI_SWIGLU) {
         uint16_t* dst = p.a_out + (size_t)slot * p.a_ld + rg * 32 + (lane >> 4) * 4;
 #pragma unroll
@@ -273,7 +301,7 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
         }
       } else if constexpr (EPI == EPI_COMBINE) {
         int f;
-        if constexpr (SET == SET_INDEXED) {
+        if constexpr (SET == SET_INDEXED || SET == SET_ROUTED) {
           f = p.sorted_ids[slot];
         } else {
           f = (p.m_indices[slot] == e) ? p.row_src[slot] : -1;
@@ -285,6 +313,15 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
         for (int mt = 0; mt < kMT; ++mt) {
           const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
           if (n < p.N) *reinterpret_cast<f32x4_t*>(dst + n) = w * acc[mt][nt];
+        }
+      } else if constexpr (EPI == EPI_PARTIAL) {
+        const int f = p.sorted_ids[slot];
+        if (f < 0 || f >= p.sentinel) continue;
+        float* dst = p.part + ((size_t)ks * p.part_rows + f) * p.N;
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+          const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
+          if (n < p.N) *reinterpret_cast<f32x4_t*>(dst + n) = acc[mt][nt];
         }
       } else {
         uint16_t* dst = p.out + (size_t)slot * p.out_ld;
@@ -698,6 +735,10 @@ hipError_t launch_nt(const GemmParams& p, int set, int epi, hipStream_t s) {
   MOE_GEMM_CASE(SET_INDEXED, EPI_SWIGLU)
   MOE_GEMM_CASE(SET_INDEXED, EPI_COMBINE)
   MOE_GEMM_CASE(SET_INDEXED, EPI_STORE)
+  MOE_GEMM_CASE(SET_INDEXED, EPI_PARTIAL)
+  MOE_GEMM_CASE(SET_ROUTED, EPI_SWIGLU)
+  MOE_GEMM_CASE(SET_ROUTED, EPI_COMBINE)
+  MOE_GEMM_CASE(SET_ROUTED, EPI_PARTIAL)
   MOE_GEMM_CASE(SET_MASKED, EPI_SWIGLU)
   MOE_GEMM_CASE(SET_MASKED, EPI_STORE)
   MOE_GEMM_CASE(SET_BLOCKS, EPI_SWIGLU)

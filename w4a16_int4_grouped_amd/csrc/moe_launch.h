@@ -21,6 +21,7 @@ enum Epilogue : int {
   EPI_SWIGLU = 0,    // W13: a[slot][c] = bf16(silu(gate) * up)
   EPI_COMBINE = 1,   // W2: yrows[f][n] = w[f] * y   (f from sorted_ids / row_src)
   EPI_STORE = 2,     // out[slot][n] = bf16(y); W13 with gate_up_I: gate columns [0, I), up [I, 2I)
+  EPI_PARTIAL = 3,   // split K: part[ks][f][n] = this split's FP32 sum (n in prepared row order)
 };
 
 struct GemmParams {
@@ -62,6 +63,11 @@ struct GemmParams {
   uint16_t* out;
   int64_t out_ld;             // STORE
   int gate_up_I;              // STORE of W13 (gate_up_I = I): un-interleave gate | up columns
+  // split K (small-M, indexed): ksplit workgroups per (set, quad), each over an
+  // equal share of the K chunks, writing FP32 partial sums part[ks][f][0, N)
+  int ksplit;
+  float* part;
+  int64_t part_rows;          // F = T * topk rows per split
 };
 
 // dispatch 1 or 2: routing blocks (SET_ROUTED, block 16*nt) only; total_wg
@@ -74,6 +80,16 @@ hipError_t launch_gemm_large_m(const GemmParams& p, int set, int epi, hipStream_
 // a[r][c] = bf16(silu(h[r][c]) * h[r][I + c]) for r < rows, c < I (I a
 // multiple of 8; h rows of 2I, a rows of I, BF16).
 hipError_t launch_swiglu(const uint16_t* h, int64_t rows, int I, uint16_t* a, hipStream_t s);
+// Split-K reductions (partials in split order, s ascending):
+//   W13: a[slot][c] = bf16(silu(sum_s g) * sum_s u) for valid routing slots,
+//        g and u at the prepared gate / up rows of column c of part [S][F][2I];
+//   W2:  out[t] = bf16(sum_j w[t,j] * sum_s part[s][t*topk + j]) over rows with
+//        slot_of >= 0 (zeros when hdr does not describe (E, block, T*topk)).
+hipError_t launch_splitk_swiglu(const float* part, int S, int64_t F, int I, const int32_t* sorted_ids,
+                                int cap, int sentinel, uint16_t* a, int64_t a_ld, hipStream_t s);
+hipError_t launch_splitk_combine(const float* part, int S, const int32_t* slot_of, const int32_t* hdr,
+                                 int E, int block, const float* topk_w, int T, int topk, int H,
+                                 uint16_t* out, hipStream_t s);
 
 // map (NULL: ids are local): device int32 [Eg], global id -> local expert
 // of this handle or -1; rows whose id maps outside [0, E) are dropped.
