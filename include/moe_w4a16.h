@@ -95,7 +95,9 @@ typedef struct {
  * measured in "H200 and Blackwell indexed decode" (semi-static against fully
  * dynamic):
  *   0  semi-static (default): a grid fixed from host-known sizes, one
- *      workgroup per (expert, 256 weight rows), row counts read on the device;
+ *      workgroup per (expert, 256 weight rows), row counts read on the device
+ *      (with fewer routed rows than experts, the grid covers T*topk sets,
+ *      each taking the next expert that holds rows);
  *   1  persistent, static: one workgroup per resident slot, each taking an
  *      equal contiguous range of (routing block, 256 weight rows) jobs;
  *   2  persistent, fully dynamic: the same workgroups taking jobs one at a
