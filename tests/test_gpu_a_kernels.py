@@ -30,6 +30,10 @@ ROUTINGS = [
     ("ragged", 7, 1001, 3, "softmax"),
     ("small-path-max", 64, 512, 8, "softmax"),   # 4096 rows: the one-workgroup path's limit
     ("chunked-path-min", 64, 513, 8, "zipf"),    # 4104 rows: the smallest multi-workgroup case
+    ("experts-513", 513, 40, 4, "softmax"),      # above the one-workgroup path's 512 experts, few rows
+    ("experts-max", 4096, 700, 8, "zipf"),       # the largest expert count a handle accepts
+    ("topk-max", 96, 64, 64, "softmax"),         # the largest top-k (64): 4096 rows
+    ("many-rows", 384, 16384, 8, "zipf"),        # 131072 rows in 128 chunks
 ]
 
 

@@ -25,6 +25,9 @@ INDEXED_CASES = [
     (16, 256, 128, 64, 4, {"block_m": 64}),
     (16, 256, 128, 64, 4, {"block_m": 128, "schedule": 1}),
     (384, 128, 64, 448, 8, None),          # config 1 routing shape, small weights
+    (1024, 128, 64, 40, 8, None),          # 320 rows over 1024 experts: grid over the active ones
+    (4096, 128, 64, 100, 8, None),         # the largest expert count a handle accepts
+    (96, 128, 64, 24, 64, None),           # the largest top-k (64)
 ]
 
 
