@@ -25,8 +25,21 @@
  *     on an error nothing is enqueued and moe_last_error() describes it.
  *   - Device-side data errors cannot be seen without a synchronisation:
  *     expert ids outside [0, E) route nowhere, masked_m is clamped to
- *     [0, max_m], and a contiguous row whose m_index is outside [0, E) is
- *     treated as padding.
+ *     [0, max_m], a contiguous row whose m_index is outside [0, E) is
+ *     treated as padding, a contiguous block takes its largest expert id
+ *     and skips rows of any other, and a routing buffer made for another
+ *     (block, E, T, topk) makes the layer compute nothing.
+ *   - MOE_W4A16_VALIDATE=1 in the environment when weights are prepared
+ *     turns those cases into errors for that handle: before enqueuing the
+ *     layer, a call checks its index data with small kernels on its stream
+ *     (topk_ids in [-1, experts), expert_map in [-1, E), masked_m in
+ *     [0, max_m], m_indices in [-1, E) with one expert per 128-row block,
+ *     row_src paired with m_indices and each flat row used once, a passed-in
+ *     routing's header), reads the counts back and synchronises the stream.
+ *     A failed check returns INVALID_ARG, or ROUTING_MISMATCH for the
+ *     routing header. The counters live in the workspace (the routing
+ *     buffer's scratch for moe_align); nothing is allocated. A debugging
+ *     aid: the synchronisation makes such calls uncapturable in a graph.
  *   - Calls that share a workspace or routing buffer on one stream are
  *     ordered by the stream; concurrent use of one buffer from two streams
  *     races.
@@ -53,7 +66,8 @@ typedef enum {
   MOE_ERR_OVERRIDE_REJECTED = 4,  /* tuning override on a grouped layout */
   MOE_ERR_WORKSPACE_TOO_SMALL = 5,/* workspace / routing / prepared buffer */
   MOE_ERR_HIP = 6,                /* a HIP runtime call failed */
-  MOE_ERR_ROUTING_MISMATCH = 7    /* routing buffer made for other shapes */
+  MOE_ERR_ROUTING_MISMATCH = 7    /* routing buffer made for other shapes
+                                     (reported in the validation mode) */
 } moe_status_t;
 
 /* Layout a set of prepared weights serves (Chord page, "Grouped SM90

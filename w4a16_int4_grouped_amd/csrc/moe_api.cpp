@@ -62,6 +62,7 @@ struct EnvOverrides {
   int no_resident = 0;   // MOE_W4A16_NO_RESIDENT: keep the K-loop form of large-M for short K
   int job_wgs = 0;       // MOE_W4A16_JOB_WGS: cap on the persistent small-M grid (tests: long job walks)
   int ksplit = 0;        // MOE_W4A16_KSPLIT: force the small-M split-K factor (tests)
+  int validate = 0;      // MOE_W4A16_VALIDATE: synchronous checks of device-side index data
   void read() {
     auto geti = [](const char* k) {
       const char* v = std::getenv(k);
@@ -73,6 +74,7 @@ struct EnvOverrides {
     no_resident = geti("MOE_W4A16_NO_RESIDENT");
     job_wgs = geti("MOE_W4A16_JOB_WGS");
     ksplit = geti("MOE_W4A16_KSPLIT");
+    validate = geti("MOE_W4A16_VALIDATE");
   }
 };
 
@@ -412,7 +414,8 @@ moe_status_t check_topk(const moe_weights_t* h, int T, int topk) {
 // the second GEMM (one per flat routed row, summed by the combine), the
 // contiguous layout's row-validity map, and the indexed layout's own routing.
 struct WsLayout {
-  size_t off_a = 0, off_y = 0, off_part = 0, off_queue = 0, off_valid = 0, off_routing = 0, total = 0;
+  size_t off_a = 0, off_y = 0, off_part = 0, off_queue = 0, off_check = 0, off_valid = 0, off_routing = 0,
+         total = 0;
 };
 
 WsLayout ws_indexed(const moe_weights_t* h, int T, int topk, int block, const Schedule& sc) {
@@ -431,6 +434,8 @@ WsLayout ws_indexed(const moe_weights_t* h, int T, int topk, int block, const Sc
   o = round_up(o + (size_t)T * topk * (p13 > p2 ? p13 : p2) * 4, kAlign);
   w.off_queue = o;   // job counters of the persistent small-M dispatch (W13, W2)
   o += kAlign;
+  w.off_check = o;   // counters of the validation mode
+  o += kAlign;
   w.off_valid = w.off_routing = o;
   o = round_up(o + (size_t)R.total_ints * 4, kAlign);
   w.total = o;
@@ -447,6 +452,8 @@ WsLayout ws_rows(const moe_weights_t* h, int64_t rows, int64_t flat_rows) {
   o = round_up(o + (size_t)flat_rows * h->desc.hidden * 4, kAlign);
   w.off_valid = w.off_routing = o;
   o = round_up(o + (size_t)flat_rows * 4, kAlign);
+  w.off_check = o;   // counters of the validation mode
+  o += kAlign;
   w.total = o;
   return w;
 }
@@ -472,6 +479,52 @@ moe_status_t set_device(const moe_weights_t* h) {
     e = hipSetDevice(h->device);
     if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
   }
+  return MOE_OK;
+}
+
+// ---- validation mode (MOE_W4A16_VALIDATE=1, read when weights are prepared)
+// The layer kernels drop or clamp bad index data without a sign; this mode
+// counts such entries with small kernels, reads the counts back and
+// synchronises the stream, and fails the call (INVALID_ARG, or
+// ROUTING_MISMATCH for a routing buffer made for another call) before the
+// layer is enqueued.
+
+// The first nonzero of n device counters fails the call with its text.
+moe_status_t read_checks(hipStream_t s, const int32_t* cnt, int n, const char* const* what) {
+  int32_t host[4] = {0, 0, 0, 0};
+  hipError_t e = hipMemcpyAsync(host, cnt, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "validation read-back");
+  for (int i = 0; i < n; ++i)
+    if (host[i]) return fail(MOE_ERR_INVALID_ARG, "validation: %d %s", host[i], what[i]);
+  return MOE_OK;
+}
+
+// Expert ids in [-1, hi) (-1: the row routes nowhere), and with an expert
+// map its entries in [-1, E). cnt: 2 device ints of scratch.
+moe_status_t validate_ids(hipStream_t s, int32_t* cnt, const int32_t* ids, int64_t n, int hi,
+                          const int32_t* map, int Eg, int E) {
+  hipError_t e = launch_zero_i32(cnt, 2, s);
+  if (e == hipSuccess) e = launch_count_outside(ids, n, -1, hi, cnt, s);
+  if (e == hipSuccess && map) e = launch_count_outside(map, Eg, -1, E, cnt + 1, s);
+  if (e != hipSuccess) return hip_fail(e, "validation launch");
+  static const char* const what[] = {"topk_ids outside [-1, experts)", "expert_map entries outside [-1, E)"};
+  return read_checks(s, cnt, map ? 2 : 1, what);
+}
+
+// A routing buffer passed in must come from moe_align / moe_align_ep for
+// this (block, E, T, topk); the kernels otherwise compute nothing.
+moe_status_t validate_routing(hipStream_t s, const void* routing, int B, int E, int T, int topk) {
+  int32_t hdr[kHdrInts];
+  hipError_t e = hipMemcpyAsync(hdr, routing, sizeof(hdr), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "validation read-back");
+  if (hdr[HDR_MAGIC] != kRoutingMagic)
+    return fail(MOE_ERR_ROUTING_MISMATCH, "validation: the routing buffer holds no alignment");
+  if (hdr[HDR_BLOCK] != B || hdr[HDR_E] != E || hdr[HDR_T] != T || hdr[HDR_TOPK] != topk)
+    return fail(MOE_ERR_ROUTING_MISMATCH,
+                "validation: routing made for block %d, E %d, T %d, topk %d; this call: %d, %d, %d, %d",
+                hdr[HDR_BLOCK], hdr[HDR_E], hdr[HDR_T], hdr[HDR_TOPK], B, E, T, topk);
   return MOE_OK;
 }
 
@@ -644,6 +697,12 @@ static moe_status_t align_impl(const moe_weights_t* h, const int32_t* topk_ids, 
                 (size_t)R.total_ints * 4);
   if ((st = set_device(h)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (h->env.validate && T > 0) {   // counters in the scratch the alignment overwrites next
+    int32_t* cnt = (int32_t*)routing + R.off_scratch;
+    if ((st = validate_ids(s, cnt, topk_ids, (int64_t)T * topk, map ? Eg : h->desc.num_experts, map, Eg,
+                           h->desc.num_experts)) != MOE_OK)
+      return st;
+  }
   hipError_t e = run("align", s, [&] {
     return launch_align(topk_ids, T, topk, h->desc.num_experts, R, (int32_t*)routing, s, map, Eg);
   });
@@ -685,6 +744,8 @@ moe_status_t moe_permute(const moe_weights_t* h, const uint16_t* x, int32_t T, i
   R.init(h->desc.num_experts, T, topk, B);
   if ((st = set_device(h)) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (h->env.validate && (st = validate_routing(s, routing, B, h->desc.num_experts, T, topk)) != MOE_OK)
+    return st;
   hipError_t e = run("permute", s, [&] {
     return launch_permute(x, T, topk, h->desc.hidden, R, (const int32_t*)routing, a_out, m_indices,
                           row_src, s);
@@ -740,6 +801,12 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   char* wsb = (char*)ws;
   RoutingLayout R;
   R.init(h->desc.num_experts, T, topk, B);
+  if (h->env.validate) {
+    st = routing ? validate_routing(s, routing, B, h->desc.num_experts, T, topk)
+                 : validate_ids(s, (int32_t*)(wsb + W.off_check), topk_ids, (int64_t)T * topk,
+                                h->desc.num_experts, nullptr, 0, h->desc.num_experts);
+    if (st != MOE_OK) return st;
+  }
   const int32_t* rt = (const int32_t*)routing;
   hipError_t e = hipSuccess;
   if (!rt) {
@@ -873,6 +940,7 @@ static moe_status_t indexed_gemm_step(const moe_weights_t* hc, int mat, const ui
   Schedule semi = sc;
   semi.dispatch = 0;   // the persistent forms serve the fused call only
   hipStream_t s = (hipStream_t)stream;
+  if (h->env.validate && (st = validate_routing(s, routing, B, E, T, topk)) != MOE_OK) return st;
   const hipError_t e = run_gemm(mat, semi, p, set, EPI_STORE, s, h->env);
   if (e != hipSuccess) return hip_fail(e, mat == 13 ? "gate_up launch" : "down launch");
   return ok();
@@ -937,6 +1005,19 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
   float* yrows = (float*)(wsb + W.off_y);
   int32_t* valid = (int32_t*)(wsb + W.off_valid);
   hipError_t e = hipSuccess;
+  if (h->env.validate) {   // the row-validity map serves as the row_src scratch
+    int32_t* cnt = (int32_t*)(wsb + W.off_check);
+    e = launch_zero_i32(cnt, 3, s);
+    if (e == hipSuccess) e = launch_count_outside(m_indices, M_pad, -1, h->desc.num_experts, cnt, s);
+    if (e == hipSuccess) e = launch_count_mixed_blocks(m_indices, M_pad, cnt + 1, s);
+    if (e == hipSuccess && row_src)
+      e = launch_count_row_src(m_indices, row_src, M_pad, T * topk, valid, cnt + 2, s);
+    if (e != hipSuccess) return hip_fail(e, "validation launch");
+    static const char* const what[] = {"m_indices outside [-1, E)",
+                                       "128-row blocks holding rows of two experts",
+                                       "rows whose row_src is out of range, repeated, or not -1 on a pad row"};
+    if ((st = read_checks(s, cnt, row_src ? 3 : 2, what)) != MOE_OK) return st;
+  }
 
   GemmParams p{};
   p.m_indices = m_indices;
@@ -1009,6 +1090,14 @@ moe_status_t moe_w4a16_masked(const moe_weights_t* hc, const uint16_t* a3, int32
 
   hipStream_t s = (hipStream_t)stream;
   char* wsb = (char*)ws;
+  if (h->env.validate) {
+    int32_t* cnt = (int32_t*)(wsb + W.off_check);
+    hipError_t ev = launch_zero_i32(cnt, 1, s);
+    if (ev == hipSuccess) ev = launch_count_outside(masked_m, h->desc.num_experts, 0, max_m + 1, cnt, s);
+    if (ev != hipSuccess) return hip_fail(ev, "validation launch");
+    static const char* const what[] = {"masked_m entries outside [0, max_m]"};
+    if ((st = read_checks(s, cnt, 1, what)) != MOE_OK) return st;
+  }
   const int H = h->desc.hidden, I = h->desc.inter, E = h->desc.num_experts;
   uint16_t* a_ws = (uint16_t*)(wsb + W.off_a);
   GemmParams p{};

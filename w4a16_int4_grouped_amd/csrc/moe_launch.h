@@ -103,6 +103,15 @@ hipError_t launch_repack(const MatLayout& m, const int32_t* words, const uint16_
 hipError_t launch_dequant_expert(const MatLayout& m, const char* prepared, int expert,
                                  uint16_t* out, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t s);
+// Data checks (MOE_W4A16_VALIDATE=1); each adds its count to *bad.
+// Entries of v[0, n) outside [lo, hi):
+hipError_t launch_count_outside(const int32_t* v, int64_t n, int lo, int hi, int32_t* bad, hipStream_t s);
+// 128-row blocks of m_indices holding two different experts:
+hipError_t launch_count_mixed_blocks(const int32_t* m_indices, int M_pad, int32_t* bad, hipStream_t s);
+// Rows whose row_src breaks the pairing with m_indices (pad <-> -1, a row's
+// source in [0, n_flat), each source used once); seen: n_flat ints of scratch.
+hipError_t launch_count_row_src(const int32_t* m_indices, const int32_t* row_src, int M_pad, int n_flat,
+                                int32_t* seen, int32_t* bad, hipStream_t s);
 // out[t] = bf16(sum over j ascending of yrows[t*topk + j]) for rows with
 // valid[t*topk + j] >= 0; tokens with no such row get 0. hdr (may be NULL):
 // routing header that must describe (E, block, T*topk), else out = 0.
