@@ -9,10 +9,12 @@ HBM when timing starts.
 
 Default workload: Kimi-K2.x-shaped decode, indexed layout (384 experts,
 hidden 7168, intermediate 2048, 448 tokens, top-8). --workload picks any of
-the five (synth.WORKLOADS).
+the eight (synth.WORKLOADS).
 
-Prints one JSON line. Per-kernel durations come from HIP events the library
-records around each launch on the launch stream during the timed steps; the
+Prints one JSON line. The K timed steps are bracketed by stream events only.
+Per-kernel durations come from K further steps during which the library
+records HIP events around each launch on the launch stream (those events add
+a few µs between launches, so they stay out of the timed steps). The
 roofline's traffic is the rocprofv3 counter measurement recorded under
 profiles/ for the same kernel and workload (null when none matches the
 current sources).
@@ -44,6 +46,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-ms", type=float, default=200.0,
+                    help="keep warming up past --warmup calls until this much wall time has passed: the "
+                         "GPU's clocks take ~50-100 ms of load to settle after idle")
     ap.add_argument("--workload", type=int, default=1,
                     help="index into synth.WORKLOADS (1: the Kimi decode layer, the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -55,6 +60,9 @@ def parse():
                          "(default), 1 persistent static ranges, 2 persistent atomic job queue, "
                          "3 semi-static grid over routing blocks")
     ap.add_argument("--cpu-experts", type=int, default=48, help="experts in the oracle's timed sample")
+    ap.add_argument("--cold-calls", type=int, default=0, metavar="N",
+                    help="after the timed steps, time N more calls one by one, each after a 1 GiB write "
+                         "that evicts the L2s and the MALL, and report their p10/p50/p90")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (steps times), the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -98,6 +106,25 @@ def measured_traffic(workload, kernel):
         if r["workload"] == workload and r["kernel"] == kernel and r["sources_sha256"] == sha:
             return r["fetch_bytes"] + r["write_bytes"]
     return None
+
+
+def cold_calls(step, stream, n):
+    """Per-call µs of n calls, each timed alone with HIP events on the call's
+    stream after a 1 GiB write that evicts the L2s and the 256 MB MALL."""
+    import numpy as np
+    import torch
+    scratch = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for i in range(n):
+            scratch.fill_(i)
+            ev[i][0].record(stream)
+            step()
+            ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return {"p10": float(np.percentile(us, 10)), "p50": float(np.percentile(us, 50)),
+            "p90": float(np.percentile(us, 90)), "calls": n, "flush_bytes": 1 << 30}
 
 
 def log(*a):
@@ -257,11 +284,20 @@ def main():
         def step():
             h.masked(a3_d, mm_d, wl.expected_m, out=out, ws=ws, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    M.profile_reset()
-    M.profile_enable(True)
+    # warmup: at least --warmup calls and --warmup-ms of wall time, in groups
+    # of 8 calls with a synchronisation after each, so that the wall time
+    # follows the GPU; the host API overhead (wall time to enqueue one call,
+    # no synchronisation) is the median over these calls
+    host_us = []
+    t_warm = time.perf_counter()
+    while len(host_us) < args.warmup or (time.perf_counter() - t_warm) * 1e3 < args.warmup_ms:
+        for _ in range(8 if len(host_us) >= args.warmup else min(8, args.warmup - len(host_us))):
+            t0 = time.perf_counter()
+            step()
+            host_us.append((time.perf_counter() - t0) * 1e6)
+        torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t_warm) * 1e3
+    # the timed steps: stream events around all K calls and nothing in between
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
@@ -269,9 +305,21 @@ def main():
         step()
     e1.record(stream)
     torch.cuda.synchronize()
-    M.profile_enable(False)
     ms = e0.elapsed_time(e1) / args.steps
+    # per-kernel durations: K more calls with the library's HIP events around
+    # each launch on its stream (the events add a few µs between launches,
+    # so they stay out of the timed steps)
+    M.profile_reset()
+    M.profile_enable(True)
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    for _ in range(args.steps):
+        step()
+    p1.record(stream)
+    torch.cuda.synchronize()
+    M.profile_enable(False)
     kernels = M.profile_read()
+    log(f"  profiled steps: {p0.elapsed_time(p1) / args.steps * 1e3:.1f} us/call (timed: {ms * 1e3:.1f})")
     log("  kernels (avg us): " + ", ".join(f"{k}={v[1] / v[0] * 1e3:.1f}" for k, v in sorted(kernels.items())))
 
     # dominant kernel: the W13 grouped GEMM. Few rows per expert: bound by HBM
@@ -322,6 +370,12 @@ def main():
         "roofline": roof,
         "kernels_avg_us": {k: v[1] / v[0] * 1e3 for k, v in kernels.items()},
     }
+    result["warmup_calls"] = len(host_us)   # --warmup, extended to --warmup-ms of wall time
+    result["warmup_ms"] = warm_ms
+    if host_us:
+        result["host_us_per_call"] = float(np.median(host_us))
+    if args.cold_calls > 0:
+        result["per_call_flushed_us"] = cold_calls(step, stream, args.cold_calls)
     if not args.no_cpu_baseline and wl.layout == "indexed":
         log("  timing the CPU oracle sample")
         result["cpu_baseline"] = cpu_baseline(wl, w, x, ids, tw, args.cpu_experts)

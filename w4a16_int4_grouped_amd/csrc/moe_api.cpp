@@ -100,7 +100,10 @@ struct Profiler {
       return e;
     }
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    // timing only: without the system-scope fence, recording an event
+    // neither writes back nor invalidates the caches, which would change
+    // the speed of the launch that follows it
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
   }
   void drain() {   // caller holds mu
