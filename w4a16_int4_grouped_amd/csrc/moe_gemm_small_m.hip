@@ -35,6 +35,8 @@
 // masked / contiguous without row_src).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -88,20 +90,23 @@ __device__ __forceinline__ void store_b(TileLds<NT>& lds, int buf, const u32x4_t
     *reinterpret_cast<u32x4_t*>(&lds.b[buf][nt][r][piece * 8]) = st[nt];
 }
 
-// One K chunk. NT = 1 (decode, 4 waves/SIMD at <= 128 registers): weight
-// tile outer, the single token fragment re-read from LDS per step. NT >= 2:
-// step outer; the step's NT token fragments stay in registers across the 4
-// weight tiles (one LDS read per token tile and step instead of four), and
-// each tile's MFMAs carry the next tile's dequantisation and, on the last
-// tile, the next step's LDS reads (issue order set by sched_group_barrier).
-template <int NT>
+// One K chunk over the first NA of the NT token tiles (a pass whose rows
+// fill fewer tiles computes only those). NA = 1 (decode, 4 waves/SIMD at
+// <= 128 registers): weight tile outer, the single token fragment re-read
+// from LDS per step. NA >= 2: step outer; the step's NA token fragments stay
+// in registers across the 4 weight tiles (one LDS read per token tile and
+// step instead of four), and each tile's MFMAs carry the next tile's
+// dequantisation and, on the last tile, the next step's LDS reads (issue
+// order set by sched_group_barrier).
+template <int NA, int NT>
 __device__ __forceinline__ void mma_chunk(const AFrag& f, const TileLds<NT>& lds, int buf,
                                           f32x4_t (&acc)[kMT][NT], uint32_t mlo,
                                           uint32_t mhi) {
+  static_assert(NA >= 1 && NA <= NT, "active token tiles");
   const int lane = threadIdx.x & 63;
   const uint16_t* brow = &lds.b[buf][0][lane & 15][(lane >> 4) * 32];
   const float sc[4] = {bf16_lo(f.S[0]), bf16_hi(f.S[0]), bf16_lo(f.S[1]), bf16_hi(f.S[1])};
-  if constexpr (NT == 1) {
+  if constexpr (NA == 1) {
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
       const GroupScale gs = group_scale(sc[mt]);
@@ -113,13 +118,13 @@ __device__ __forceinline__ void mma_chunk(const AFrag& f, const TileLds<NT>& lds
       }
     }
   } else {
-    constexpr int kValu = (17 + NT - 1) / NT;
+    constexpr int kValu = (17 + NA - 1) / NA;
     GroupScale gs[kMT];
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) gs[mt] = group_scale(sc[mt]);
-    u32x4_t bf[NT];
+    u32x4_t bf[NA];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) bf[nt] = *reinterpret_cast<const u32x4_t*>(brow + nt * (16 * kBRow));
+    for (int nt = 0; nt < NA; ++nt) bf[nt] = *reinterpret_cast<const u32x4_t*>(brow + nt * (16 * kBRow));
     u32x4_t a = dq8(f.A[0][0], gs[0], mlo, mhi);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -130,13 +135,13 @@ __device__ __forceinline__ void mma_chunk(const AFrag& f, const TileLds<NT>& lds
         u32x4_t an = a;
         if (ng < 4) an = dq8(f.A[nmt][ng], gs[nmt], mlo, mhi);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int nt = 0; nt < NA; ++nt) {
           acc[mt][nt] = mfma16(a, bf[nt], acc[mt][nt]);
           if (last && g < 3)
             bf[nt] = *reinterpret_cast<const u32x4_t*>(brow + nt * (16 * kBRow) + (g + 1) * 8);
         }
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
+        for (int i = 0; i < NA; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
           if (last && g < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
           __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);                // VALU
@@ -257,7 +262,10 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
 
     // step J computes chunk c from register buffer J and LDS buffer J, and
     // prefetches chunk c+2 into register buffer (J+2)%3 and the token tile of
-    // chunk c+1 into LDS buffer (J+1)%3.
+    // chunk c+1 into LDS buffer (J+1)%3. The MFMAs cover the pass's first NA
+    // token tiles, those that hold rows (the token loads stay whole).
+    auto k_loop = [&](auto na) __attribute__((always_inline)) {
+      constexpr int NA = decltype(na)::value;
 #define MOE_SMALL_M_STEP(J, CUR, NXT2)                                                           \
   {                                                                                              \
     const int c = kc + J;                                                                        \
@@ -266,17 +274,31 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
     load_a(NXT2, more ? wq + (size_t)(c + 2) * cstride * (kMT * 64) : wq_dummy,                  \
            more ? ws + (size_t)(c + 2) * cstride * 64 : ws_dummy, lane);                         \
     __builtin_amdgcn_sched_barrier(0);                                                           \
-    if (c < Kc) mma_chunk<NT>(CUR, lds, J, acc, mlo, mhi);                                          \
+    if (c < Kc) mma_chunk<NA, NT>(CUR, lds, J, acc, mlo, mhi);                                   \
     __builtin_amdgcn_sched_barrier(0);                                                           \
     store_b<NT>(lds, (J + 1) % 3, st);                                                           \
     __syncthreads();                                                                             \
   }
-    for (int kc = 0; kc < Kc; kc += 3) {
-      MOE_SMALL_M_STEP(0, fr0, fr2)
-      MOE_SMALL_M_STEP(1, fr1, fr0)
-      MOE_SMALL_M_STEP(2, fr2, fr1)
-    }
+      for (int kc = 0; kc < Kc; kc += 3) {
+        MOE_SMALL_M_STEP(0, fr0, fr2)
+        MOE_SMALL_M_STEP(1, fr1, fr0)
+        MOE_SMALL_M_STEP(2, fr2, fr1)
+      }
 #undef MOE_SMALL_M_STEP
+    };
+    // NT = 2 keeps one body: a second one does not fit its 168 registers
+    // (3 workgroups per CU) without spilling; nor do four in the contiguous
+    // blocks' BF16 store variant, whose rows are 128-row blocks anyway
+    const int nta = min(NT, (count - tb + 15) >> 4);   // uniform: count is the set's
+    if constexpr (NT == 1 || NT == 2 || SET == SET_BLOCKS) {
+      k_loop(std::integral_constant<int, NT>{});
+    } else {
+      static_assert(NT == 4, "token tiles per pass: 1, 2 or 4");
+      if (nta == 1) k_loop(std::integral_constant<int, 1>{});
+      else if (nta == 2) k_loop(std::integral_constant<int, 2>{});
+      else if (nta == 3) k_loop(std::integral_constant<int, 3>{});
+      else k_loop(std::integral_constant<int, 4>{});
+    }
     if (!active) continue;
 
     // ---- epilogue
@@ -670,7 +692,7 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m_jobs
       load_a(NXT2, wqb + (size_t)wc * kCh, wsb + (size_t)wc * 64, lane);                      \
     }                                                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                        \
-    mma_chunk<NT>(CUR, lds, J, acc, mlo, mhi);                                                \
+    mma_chunk<NT, NT>(CUR, lds, J, acc, mlo, mhi);                                            \
     __builtin_amdgcn_sched_barrier(0);                                                        \
     if (++c == Kc) {                                                                          \
       if (cur.active) job_epilogue<NT, SET, EPI>(p, acc, cur, ef, lane);                      \
