@@ -158,6 +158,24 @@ MULTI_BLOCK_CASES = [
 ]
 
 
+WIDE_CASES = [
+    # K = 512 on both GEMMs (4 chunks: whole chunk pairs) so that the 256-row
+    # form runs both; Zipf-skewed experts give full same-expert block pairs,
+    # pairs split between two experts and partial last blocks
+    (6, 512, 512, 800, 3, "indexed", True),
+    (5, 512, 512, 700, 2, "contiguous", True),
+    (5, 512, 512, 700, 2, "contiguous", False),
+]
+
+
+@pytest.mark.parametrize("E,H,I,T,topk,layout,with_src", WIDE_CASES)
+def test_wide_tiles(E, H, I, T, topk, layout, with_src, monkeypatch):
+    """The 256-row-tile large-M K loop (MOE_W4A16_WIDE=1, read at prepare)
+    against the oracle, every epilogue."""
+    monkeypatch.setenv("MOE_W4A16_WIDE", "1")
+    test_multi_block_experts(E, H, I, T, topk, layout, with_src)
+
+
 @pytest.mark.parametrize("E,H,I,T,topk,layout,with_src", MULTI_BLOCK_CASES)
 def test_multi_block_experts(E, H, I, T, topk, layout, with_src):
     """Large-M K-loop GEMMs on experts spanning many 128-row blocks, every

@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["moe_api.cpp", "moe_align.hip", "moe_prepare.hip", "moe_gemm_small_m.hip",
-           "moe_gemm_large_m.hip", "moe_combine.hip", "moe_check.hip"]
+           "moe_gemm_large_m.hip", "moe_combine.hip", "moe_check.hip", "moe_gemm_wide.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in generated code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -63,6 +63,7 @@ struct EnvOverrides {
   int job_wgs = 0;       // MOE_W4A16_JOB_WGS: cap on the persistent small-M grid (tests: long job walks)
   int ksplit = 0;        // MOE_W4A16_KSPLIT: force the small-M split-K factor (tests)
   int validate = 0;      // MOE_W4A16_VALIDATE: synchronous checks of device-side index data
+  int wide = 0;          // MOE_W4A16_WIDE: large-M K loop over 256-row tiles (two blocks of an expert)
   void read() {
     auto geti = [](const char* k) {
       const char* v = std::getenv(k);
@@ -75,6 +76,7 @@ struct EnvOverrides {
     job_wgs = geti("MOE_W4A16_JOB_WGS");
     ksplit = geti("MOE_W4A16_KSPLIT");
     validate = geti("MOE_W4A16_VALIDATE");
+    wide = geti("MOE_W4A16_WIDE");
   }
 };
 
@@ -206,6 +208,11 @@ hipError_t run_gemm(int mat, const Schedule& sc, const GemmParams& p0, int set, 
       p.qpw = (nquads + wgs - 1) / wgs;
       p.wg_per_set = (nquads + p.qpw - 1) / p.qpw;
       p.total_wg = p.nsets * p.wg_per_set;
+    }
+    if (env.wide && p.qpw == 0 && set != SET_MASKED && p.Kc % 2 == 0) {   // K loop over pairs of blocks
+      p.total_wg = (p.nsets + 1) / 2 * p.wg_per_set;
+      return run(mat == 13 ? "gemm_w13_large_m" : "gemm_w2_large_m", s,
+                 [&] { return launch_gemm_wide(p, set, epi, s); });
     }
     return run(mat == 13 ? "gemm_w13_large_m" : "gemm_w2_large_m", s,
                [&] { return launch_gemm_large_m(p, set, epi, s); });

@@ -103,6 +103,9 @@ hipError_t launch_repack(const MatLayout& m, const int32_t* words, const uint16_
 hipError_t launch_dequant_expert(const MatLayout& m, const char* prepared, int expert,
                                  uint16_t* out, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t s);
+// Large-M K loop over 256-row tiles (pairs of 128-row routing or contiguous
+// blocks of one expert); p.total_wg = ceil(nsets / 2) * wg_per_set.
+hipError_t launch_gemm_wide(const GemmParams& p, int set, int epi, hipStream_t s);
 // Data checks (MOE_W4A16_VALIDATE=1); each adds its count to *bad.
 // Entries of v[0, n) outside [lo, hi):
 hipError_t launch_count_outside(const int32_t* v, int64_t n, int lo, int hi, int32_t* bad, hipStream_t s);
