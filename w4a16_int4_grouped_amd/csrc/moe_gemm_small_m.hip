@@ -279,10 +279,18 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
     store_b<NT>(lds, (J + 1) % 3, st);                                                           \
     __syncthreads();                                                                             \
   }
-      for (int kc = 0; kc < Kc; kc += 3) {
+      // whole rotations, then the one or two chunks left (no step past the
+      // last chunk pays for loads and a barrier)
+      const int Kc3 = Kc - Kc % 3;
+      int kc = 0;
+      for (; kc < Kc3; kc += 3) {
         MOE_SMALL_M_STEP(0, fr0, fr2)
         MOE_SMALL_M_STEP(1, fr1, fr0)
         MOE_SMALL_M_STEP(2, fr2, fr1)
+      }
+      if (kc < Kc) {
+        MOE_SMALL_M_STEP(0, fr0, fr2)
+        if (kc + 1 < Kc) MOE_SMALL_M_STEP(1, fr1, fr0)
       }
 #undef MOE_SMALL_M_STEP
     };
