@@ -29,10 +29,7 @@
 // copies removed ran 22 % faster than the 128-row kernel, so the copies and
 // their barriers, not the MFMAs, bound this form.
 //
-// A half-chunk stage holds, for each 16-row block nt and lane quarter q, the
-// 16 rows' pieces of MFMA steps 2h and 2h + 1 (8 k each): slot
-// ((nt*4 + q)*16 + r)*2 + (j ^ (r >> 3 & 1)), which keeps the 16-byte
-// fragment reads of a quarter (16 rows, 32 B apart) on distinct banks.
+// The half-chunk stage layout and its copies are described in moe_tile.h.
 //
 // Row sets: routing blocks (indexed, block 128) or 128-row contiguous
 // blocks, paired as (2i, 2i+1); a pair whose blocks belong to two experts is
@@ -72,43 +69,11 @@ __device__ __forceinline__ void load_w(WFrag& f, const u32x4_t* __restrict__ wq,
   f.S = __builtin_nontemporal_load(ws + 2 * lane);
 }
 
-// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left free)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 // Keeps a loaded value where it is used: the empty asm "changes" it, and
 // volatile asm keeps its place among the barriers, so no consumer of the
 // value is hoisted above the wait that covers its load.
 __device__ __forceinline__ void pin(WFrag& f) {
   asm volatile("" : "+v"(f.A[0]), "+v"(f.A[1]), "+v"(f.S));
-}
-
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// This wave's share of stage s (chunk s/2, half s%2) of the token tile, copied
-// straight from global memory to LDS: its 32 rows (16-row blocks 2*wave,
-// 2*wave + 1), four 16-byte pieces per lane. src[i]: the lane's row pointer
-// for block 2*wave + i at k = 0. Lane l's piece i goes to stage slot
-// (4*wave + i)*64 + l: block 2*wave + i/2, quarter q = (2i + l/32) % 4, row
-// r = (l/2) % 16, position l % 2 holding step j = (l % 2) ^ (r / 8 % 2).
-__device__ __forceinline__ void dma_stage(u32x4_t* stage, const char* const (&src)[2], int s, int wave,
-                                          int lane) {
-  const int kc = s >> 1, h = s & 1;
-  const int r = (lane >> 1) & 15;
-  const int j = (lane & 1) ^ ((r >> 3) & 1);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = (2 * i + (lane >> 5)) & 3;
-    const char* g = src[i >> 1] + (size_t)kc * (kKC * 2) + q * 64 + h * 32 + j * 16;
-    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(stage + (4 * wave + i) * 64), 16, 0, 0);
-  }
 }
 
 // Two MFMA steps (one stage) over the first NT token tiles.
@@ -224,18 +189,19 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, const WideCtx& c,
   // last one (every wave loads its share unconditionally: a branch around the
   // loads would make the compiler wait for all of them before the LDS reads)
   const bool gather = SET == SET_ROUTED && p.gather;
-  const char* src[2];
+  uint32_t rowb[2];   // byte offsets of the rows in the token matrix
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int r = 32 * wave + 16 * i + ((lane >> 1) & 15);
+    const int r = stage_row(wave, i, lane);
     const int slot = c.slot0 + min(r, rows - 1);
     int row = slot;
     if (gather) {
       const int f = p.sorted_ids[slot];
       row = (f >= 0 && f < p.sentinel) ? f / p.topk : 0;   // pad slots read row 0
     }
-    src[i] = reinterpret_cast<const char*>(p.src + (size_t)row * p.src_ld);
+    rowb[i] = (uint32_t)row * (uint32_t)p.src_ld * 2u;
   }
+  const StageSrc src = stage_src(p.src, rowb[0], rowb[1], lane);
   const int NS = 2 * p.Kc;   // stages
   f32x4_t acc[2][NT];
 #pragma unroll
@@ -252,9 +218,13 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, const WideCtx& c,
   // the end of iteration t-2, waited for at the top of iteration t)
   WFrag fw[2];
   stage_barrier();   // the previous tile's readers are done with the ring
-  dma_stage(lds.s[0], src, 0, wave, lane);
+  // issued in this order (the waits below count on it)
+  dma_stage(lds.s[0], src, 0, wave);
+  __builtin_amdgcn_sched_barrier(0);
   load_w(fw[0], wq_at(0), ws_at(0), lane);
-  dma_stage(lds.s[1], src, 1, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  dma_stage(lds.s[1], src, 1, wave);
+  __builtin_amdgcn_sched_barrier(0);
 
   // Loads issued after those iteration s needs: s even (needs DMA(s), W(c)):
   // DMA(s+1); s odd (needs DMA(s)): W(c+1), DMA(s+1).
@@ -271,16 +241,20 @@ __device__ __forceinline__ void wide_tile(const GemmParams& p, const WideCtx& c,
       pin(fw[CUR]);                                                                           \
       GroupScale gs[2] = {group_scale(bf16_lo(fw[CUR].S)), group_scale(bf16_hi(fw[CUR].S))};  \
       mma_stage<NT>(fw[CUR], lds.s[(SS) & 3], (SS) & 1, c.rd, acc, gs);                      \
-      dma_stage(lds.s[((SS) + 2) & 3], src, s + 2 < NS ? s + 2 : 0, wave, lane);              \
+      dma_stage(lds.s[((SS) + 2) & 3], src, s + 2 < NS ? s + 2 : 0, wave);                    \
       __builtin_amdgcn_sched_barrier(0);   /* no work moves across stages */                  \
     }                                                                                         \
   }
-  for (int s0 = 0; s0 < NS; s0 += 4) {
+  // a do-while: with a branch around the loop the compiler sinks the
+  // weight loads above into it, past the copies the waits count on
+  int s0 = 0;
+  do {
     MOE_WIDE_ITER(0, 0, 1)
     MOE_WIDE_ITER(1, 0, 1)
     MOE_WIDE_ITER(2, 1, 0)
     MOE_WIDE_ITER(3, 1, 0)
-  }
+    s0 += 4;
+  } while (s0 < NS);
 #undef MOE_WIDE_ITER
   wait_vm<0>();   // the loads past the end land before their registers are dropped
   if (c.active) wide_epilogue<SET, EPI, NT>(p, c, rows, acc);
@@ -366,7 +340,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide(const GemmParams p) {
   c.active = rg_raw < p.RG;
   c.rg = c.active ? rg_raw : p.RG - 1;
   c.mt0 = 2 * (c.wave & 1);
-  c.rd = (lane >> 4) * 32 + (lane & 15) * 2 + ((lane >> 3) & 1);
+  c.rd = stage_rd(lane);
 
   int e0, n0, e1, n1;
   block_info<SET>(p, 2 * pair, nblocks, lane, e0, n0);
@@ -400,6 +374,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide(const GemmParams p) {
 hipError_t launch_gemm_wide(const GemmParams& p, int set, int epi, hipStream_t s) {
   if (p.total_wg <= 0) return hipSuccess;
   if (p.K % (2 * kKC)) return hipErrorInvalidValue;   // whole chunk pairs only
+  if (!src_fits_u32(p, set)) return hipErrorInvalidValue;
   if (set == SET_BLOCKS && p.block_rows != kBM1) return hipErrorInvalidValue;
   if (set == SET_ROUTED && p.block != kBM1) return hipErrorInvalidValue;
   const dim3 grid(p.total_wg), block(512);

@@ -70,6 +70,20 @@ struct GemmParams {
   int64_t part_rows;          // F = T * topk rows per split
 };
 
+// Rows of the B operand matrix a GEMM may read, for each row set kind.
+inline int64_t src_rows(const GemmParams& p, int set) {
+  if (set == SET_ROUTED) return p.gather ? (int64_t)p.sentinel / (p.topk > 0 ? p.topk : 1) : (int64_t)p.nsets * p.block;
+  if (set == SET_MASKED) return (int64_t)p.E * p.max_m;
+  return (int64_t)p.nsets * p.block_rows;
+}
+
+// The half-chunk ring K loop (256-row tiles) addresses token rows by 32-bit
+// byte offsets: the B operand matrix must span less than 4 GiB.
+inline bool src_fits_u32(const GemmParams& p, int set) {
+  const int64_t rows = src_rows(p, set);
+  return rows <= 0 || (rows - 1) * p.src_ld * 2 + (int64_t)p.K * 2 <= (int64_t)0xFFFFFFFF;
+}
+
 // dispatch 1 or 2: routing blocks (SET_ROUTED, block 16*nt) only; total_wg
 // workgroups, enough that a static range spans at most 64 blocks.
 hipError_t launch_gemm_small_m(const GemmParams& p, int set, int epi, int nt, hipStream_t s);
