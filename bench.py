@@ -35,7 +35,7 @@ METRIC = "MoE layer µs/call; decode weight GB/s & prefill TFLOP/s as % of roofl
 # HBM traffic of the dominant kernel as measured with rocprofv3 TCC counters
 # (profiles/); reported only while the sources it was measured on are unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-TRAFFIC_SOURCES = ["moe_gemm_small_m.hip", "moe_gemm_large_m.hip", "moe_device.h", "moe_layout.h",
+TRAFFIC_SOURCES = ["moe_gemm_small_m.hip", "moe_gemm_large_m.hip", "moe_device.h", "moe_layout.h", "moe_tile.h",
                    "moe_launch.h", "moe_api.cpp"]
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense BF16 MFMA
