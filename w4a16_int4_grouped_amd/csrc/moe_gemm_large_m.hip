@@ -30,6 +30,8 @@
 // its valid rows). Epilogues as in the small-M kernel.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_launch.h"
 #include "moe_tile.h"
@@ -385,6 +387,23 @@ __device__ __forceinline__ void run_tile_res(const GemmParams& p, const TileCtx&
   }
 }
 
+// Calls f(std::integral_constant<int, NTE>) with NTE = ceil(rows / 16), the
+// 16-row token tiles a tile of `rows` rows (1 .. 128) computes: each count
+// is a complete body, and a tile pays at most 15 padding rows of MFMAs.
+template <typename F>
+__device__ __forceinline__ void with_token_tiles(int rows, F&& f) {
+  switch ((rows + 15) >> 4) {
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 3: f(std::integral_constant<int, 3>{}); break;
+    case 4: f(std::integral_constant<int, 4>{}); break;
+    case 5: f(std::integral_constant<int, 5>{}); break;
+    case 6: f(std::integral_constant<int, 6>{}); break;
+    case 7: f(std::integral_constant<int, 7>{}); break;
+    default: f(std::integral_constant<int, 8>{}); break;
+  }
+}
+
 // KCR = 0: K-loop form, one quad of row groups per workgroup. KCR = 1 or 2
 // (K = 128 * KCR): K-resident form, p.qpw quads per workgroup.
 template <int SET, int EPI, int KCR>
@@ -463,25 +482,13 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m(const GemmParams p) {
     const int q0 = wgi * p.qpw, q1 = min(q0 + p.qpw, (p.RG + 3) / 4);
     if (q0 >= q1) return;
     const int rows = n_eff;
-    if (rows <= 32)
-      run_tile_res<SET, EPI, 2, KCR>(p, c, lds, meta, rows, q0, q1);
-    else if (rows <= 64)
-      run_tile_res<SET, EPI, 4, KCR>(p, c, lds, meta, rows, q0, q1);
-    else if (rows <= 96)
-      run_tile_res<SET, EPI, 6, KCR>(p, c, lds, meta, rows, q0, q1);
-    else
-      run_tile_res<SET, EPI, 8, KCR>(p, c, lds, meta, rows, q0, q1);
+    with_token_tiles(rows, [&](auto nte) {
+      run_tile_res<SET, EPI, decltype(nte)::value, KCR>(p, c, lds, meta, rows, q0, q1);
+    });
   } else {
     for (int tb = 0; tb < c.count; tb += kBM) {
       const int rows = SET == SET_MASKED ? min(c.count - tb, kBM) : n_eff;   // uniform
-      if (rows <= 32)
-        run_tile<SET, EPI, 2>(p, c, lds, tb, rows);
-      else if (rows <= 64)
-        run_tile<SET, EPI, 4>(p, c, lds, tb, rows);
-      else if (rows <= 96)
-        run_tile<SET, EPI, 6>(p, c, lds, tb, rows);
-      else
-        run_tile<SET, EPI, 8>(p, c, lds, tb, rows);
+      with_token_tiles(rows, [&](auto nte) { run_tile<SET, EPI, decltype(nte)::value>(p, c, lds, tb, rows); });
     }
   }
 }
