@@ -1,8 +1,9 @@
 // Top-k-weighted combine: out[t] = sum_j w[t, j] * y(t, j) (reading of the
 // layer's combine: the routing weight applies after the second GEMM).
 //
-// The second GEMM stores each routed row already weighted, w * y, in FP32 at
-// its flat index f = t*topk + j. This kernel adds a token's top-k rows in
+// The second GEMM stores each routed row already weighted, w * y, at its flat
+// index f = t*topk + j, as 24-bit floats (store_y24: FP32 rounded to 16
+// significant bits). This kernel adds a token's top-k rows in FP32 in
 // ascending j and rounds once to BF16. No atomics: the accumulator of an
 // atomic scatter-add is shared by workgroups on all XCDs, so every add would
 // be performed past the per-XCD L2 at a fraction of the streaming rate.
@@ -30,17 +31,16 @@ __device__ __forceinline__ f32x4_t keep_if(f32x4_t y, bool v) {
 // contiguous layout's rows). With a routing header that does not describe
 // (E, block, T*topk) nothing was computed and the result is zero, as for the
 // GEMMs. A token's rows are loaded kRowBatch at a time before any is added,
-// so a thread keeps up to 8 loads in flight instead of one (measured on the
-// TP8 shard's 940 MB of rows: 176 -> 170 us, 5.9 TB/s, against 6.6 TB/s for
-// a read-only stream). Rows still add in ascending j; a skipped row (another
+// so a thread keeps up to 8 rows' loads in flight instead of one. Rows still add in ascending j; a skipped row (another
 // GPU's expert) costs no read and adds nothing (the sum starts at +0 and
 // never becomes -0, so adding +0 is exact).
 constexpr int kRowBatch = 8;
 
-__global__ __launch_bounds__(256) void combine_rows(const f32x4_t* __restrict__ yrows,
+__global__ __launch_bounds__(256) void combine_rows(const uint16_t* __restrict__ yhi,
+                                                    const uint8_t* __restrict__ ylo,
                                                     const int32_t* __restrict__ valid,
                                                     const int32_t* __restrict__ hdr, int E, int block,
-                                                    int T, int topk, int H4,
+                                                    int T, int topk, int H4, int ld,
                                                     u32x2_t* __restrict__ out) {
   const int t = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void combine_rows(const f32x4_t* __restrict__ 
 #pragma unroll
       for (int u = 0; u < kRowBatch; ++u) {
         y[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (use[u]) y[u] = __builtin_nontemporal_load(yrows + (size_t)(f0 + j0 + u) * H4 + c);
+        if (use[u]) y[u] = load_y24(yhi, ylo, (size_t)(f0 + j0 + u) * ld, 4 * c);
       }
 #pragma unroll
       for (int u = 0; u < kRowBatch; ++u) acc += y[u];
@@ -217,13 +217,14 @@ hipError_t launch_splitk_combine(const float* part, int S, const int32_t* slot_o
   return hipGetLastError();
 }
 
-hipError_t launch_combine_rows(const float* yrows, const int32_t* valid, const int32_t* hdr, int E,
-                               int block, int T, int topk, int H, uint16_t* out, hipStream_t s) {
+hipError_t launch_combine_rows(const uint16_t* yhi, const uint8_t* ylo, int ld, const int32_t* valid,
+                               const int32_t* hdr, int E, int block, int T, int topk, int H, uint16_t* out,
+                               hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  if (ld % 64 || ld < H) return hipErrorInvalidValue;   // rows in 64-feature blocks (y24_pos)
   const int H4 = H / 4;
-  hipLaunchKernelGGL(combine_rows, dim3((H4 + 255) / 256, T), dim3(256), 0, s,
-                     reinterpret_cast<const f32x4_t*>(yrows), valid, hdr, E, block, T, topk, H4,
-                     reinterpret_cast<u32x2_t*>(out));
+  hipLaunchKernelGGL(combine_rows, dim3((H4 + 255) / 256, T), dim3(256), 0, s, yhi, ylo, valid, hdr, E, block,
+                     T, topk, H4, ld, reinterpret_cast<u32x2_t*>(out));
   return hipGetLastError();
 }
 

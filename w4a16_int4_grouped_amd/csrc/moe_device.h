@@ -183,4 +183,62 @@ __device__ __forceinline__ float swiglu(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
+// Weighted rows w*y of the second GEMM, kept for the combine as 24-bit
+// floats: the FP32 value rounded to its upper 24 bits (sign, exponent and
+// 15 stored mantissa bits, to nearest with ties away from zero), split into
+// a 16-bit high plane and an 8-bit low plane of [rows][ld] each. Each value
+// is then within 2^-16 of the FP32 one in relative terms (the layer's BF16
+// output rounds at 2^-9), and a row costs 3 bytes per feature instead of 4
+// in the GEMM's writes and the combine's reads.
+//
+// Within each 64-feature block (one row group of 4 MFMA tiles), feature
+// n = 16*mt + 4*q + i sits at position 16*q + 4*mt + i: the 16 values a lane
+// q holds for a token row (4 per tile mt) are adjacent, so a lane writes
+// them with full 16-byte stores and the 4 lanes of a row fill 128 bytes of
+// the high plane (with plain [n] order each lane would write 8- and 4-byte
+// pieces 32 bytes apart, which measured 40 % slower on the TP8 shard's W2).
+__device__ __forceinline__ int y24_pos(int n) {
+  return (n & ~63) | (((n >> 2) & 3) << 4) | (((n >> 4) & 3) << 2) | (n & 3);
+}
+
+// Stores G groups of 4 values (tiles mt0 .. mt0 + G - 1 of lane q) at row
+// element idx = block + 16*q + 4*mt0 (G = 4: mt0 = 0; G = 2: mt0 even).
+template <int G>
+__device__ __forceinline__ void store_y24(uint16_t* __restrict__ hi, uint8_t* __restrict__ lo, size_t idx,
+                                          const f32x4_t (&v)[G]) {
+  static_assert(G == 2 || G == 4, "2 or 4 groups");
+  uint32_t h[2 * G], l[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    uint32_t b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = __float_as_uint(v[g][i]) + 0x80u;
+    h[2 * g] = (b[0] >> 16) | (b[1] & 0xFFFF0000u);
+    h[2 * g + 1] = (b[2] >> 16) | (b[3] & 0xFFFF0000u);
+    l[g] = ((b[0] >> 8) & 0xFFu) | (b[1] & 0xFF00u) | ((b[2] & 0xFF00u) << 8) | ((b[3] & 0xFF00u) << 16);
+  }
+#pragma unroll
+  for (int k = 0; k < G / 2; ++k)
+    *reinterpret_cast<u32x4_t*>(hi + idx + 8 * k) = u32x4_t{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
+  if constexpr (G == 4)
+    *reinterpret_cast<u32x4_t*>(lo + idx) = u32x4_t{l[0], l[1], l[2], l[3]};
+  else
+    *reinterpret_cast<u32x2_t*>(lo + idx) = u32x2_t{l[0], l[1]};
+}
+
+// Features n0 .. n0 + 3 (n0 a multiple of 4) of a row stored by store_y24
+// (row element offset row0), as FP32.
+__device__ __forceinline__ f32x4_t load_y24(const uint16_t* __restrict__ hi, const uint8_t* __restrict__ lo,
+                                            size_t row0, int n0) {
+  const size_t idx = row0 + y24_pos(n0);
+  const u32x2_t h = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(hi + idx));
+  const uint32_t l = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(lo + idx));
+  f32x4_t v;
+  v[0] = __uint_as_float((h[0] << 16) | ((l & 0xFFu) << 8));
+  v[1] = __uint_as_float((h[0] & 0xFFFF0000u) | (l & 0xFF00u));
+  v[2] = __uint_as_float((h[1] << 16) | ((l >> 8) & 0xFF00u));
+  v[3] = __uint_as_float((h[1] & 0xFFFF0000u) | ((l >> 16) & 0xFF00u));
+  return v;
+}
+
 }  // namespace moe

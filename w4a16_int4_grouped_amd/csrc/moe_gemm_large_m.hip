@@ -212,11 +212,11 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c, 
       }
       if (f < 0 || f >= p.sentinel) continue;
       const float w = p.topk_w[f];
-      float* dst = p.yrows + (size_t)f * p.yrows_ld;
+      if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (y24_pos)
+        f32x4_t v[kMT];
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
-        const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
-        if (n < p.N) *reinterpret_cast<f32x4_t*>(dst + n) = w * acc[mt][nt];
+        for (int mt = 0; mt < kMT; ++mt) v[mt] = w * acc[mt][nt];
+        store_y24<kMT>(p.yhi, p.ylo, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, v);
       }
     } else {
       if constexpr (SET == SET_ROUTED) {
@@ -287,11 +287,11 @@ __device__ __forceinline__ void epilogue_meta(const GemmParams& p, const TileCtx
       }
     } else if constexpr (EPI == EPI_COMBINE) {
       const float w = m.w[r];
-      float* dst = p.yrows + (size_t)f * p.yrows_ld;
+      if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (y24_pos)
+        f32x4_t v[kMT];
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
-        const int n = rg * kRowsRG + mt * 16 + (lane >> 4) * 4;
-        if (n < p.N) *reinterpret_cast<f32x4_t*>(dst + n) = w * acc[mt][nt];
+        for (int mt = 0; mt < kMT; ++mt) v[mt] = w * acc[mt][nt];
+        store_y24<kMT>(p.yhi, p.ylo, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, v);
       }
     } else {
       uint16_t* dst = p.out + (size_t)slot * p.out_ld;

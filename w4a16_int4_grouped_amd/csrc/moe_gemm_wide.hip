@@ -157,11 +157,9 @@ __device__ __forceinline__ void wide_epilogue(const GemmParams& p, const WideCtx
       v[1] = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
       *reinterpret_cast<u32x2_t*>(dst) = v;
     } else if constexpr (EPI == EPI_COMBINE) {
-      float* dst = p.yrows + (size_t)fv[nt] * p.yrows_ld;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int n = c.rg * kRowsRG + (c.mt0 + t) * 16 + (lane >> 4) * 4;
-        if (n < p.N) *reinterpret_cast<f32x4_t*>(dst + n) = wv[nt] * acc[t][nt];
+      if (c.rg * kRowsRG < p.N) {   // tiles mt0, mt0 + 1 of the row group, lane-contiguous (y24_pos)
+        const f32x4_t v[2] = {wv[nt] * acc[0][nt], wv[nt] * acc[1][nt]};
+        store_y24<2>(p.yhi, p.ylo, (size_t)fv[nt] * p.yrows_ld + c.rg * kRowsRG + (lane >> 4) * 16 + c.mt0 * 4, v);
       }
     } else {
       uint16_t* dst = p.out + (size_t)slot * p.out_ld;
