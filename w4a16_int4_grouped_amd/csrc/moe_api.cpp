@@ -209,7 +209,8 @@ hipError_t run_gemm(int mat, const Schedule& sc, const GemmParams& p0, int set, 
       p.wg_per_set = (nquads + p.qpw - 1) / p.qpw;
       p.total_wg = p.nsets * p.wg_per_set;
     }
-    if (env.wide && p.qpw == 0 && set != SET_MASKED && p.Kc % 2 == 0 && src_fits_u32(p, set)) {   // K loop over pairs of blocks
+    // K loop over pairs of blocks
+    if (env.wide && p.qpw == 0 && set != SET_MASKED && p.Kc % 2 == 0 && src_fits_u32(p, set)) {
       p.total_wg = (p.nsets + 1) / 2 * p.wg_per_set;
       return run(mat == 13 ? "gemm_w13_large_m" : "gemm_w2_large_m", s,
                  [&] { return launch_gemm_wide(p, set, epi, s); });

@@ -31,9 +31,10 @@ __device__ __forceinline__ f32x4_t keep_if(f32x4_t y, bool v) {
 // contiguous layout's rows). With a routing header that does not describe
 // (E, block, T*topk) nothing was computed and the result is zero, as for the
 // GEMMs. A token's rows are loaded kRowBatch at a time before any is added,
-// so a thread keeps up to 8 rows' loads in flight instead of one. Rows still add in ascending j; a skipped row (another
-// GPU's expert) costs no read and adds nothing (the sum starts at +0 and
-// never becomes -0, so adding +0 is exact).
+// so a thread keeps up to 8 rows' loads in flight instead of one. Rows still
+// add in ascending j; a skipped row (another GPU's expert) costs no read and
+// adds nothing (the sum starts at +0 and never becomes -0, so adding +0 is
+// exact).
 constexpr int kRowBatch = 8;
 
 __global__ __launch_bounds__(256) void combine_rows(const uint16_t* __restrict__ yhi,

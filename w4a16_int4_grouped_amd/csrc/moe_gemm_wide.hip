@@ -159,7 +159,8 @@ __device__ __forceinline__ void wide_epilogue(const GemmParams& p, const WideCtx
     } else if constexpr (EPI == EPI_COMBINE) {
       if (c.rg * kRowsRG < p.N) {   // tiles mt0, mt0 + 1 of the row group, lane-contiguous (y24_pos)
         const f32x4_t v[2] = {wv[nt] * acc[0][nt], wv[nt] * acc[1][nt]};
-        store_y24<2>(p.yhi, p.ylo, (size_t)fv[nt] * p.yrows_ld + c.rg * kRowsRG + (lane >> 4) * 16 + c.mt0 * 4, v);
+        const size_t idx = (size_t)fv[nt] * p.yrows_ld + c.rg * kRowsRG + (lane >> 4) * 16 + c.mt0 * 4;
+        store_y24<2>(p.yhi, p.ylo, idx, v);
       }
     } else {
       uint16_t* dst = p.out + (size_t)slot * p.out_ld;

@@ -73,7 +73,8 @@ struct GemmParams {
 
 // Rows of the B operand matrix a GEMM may read, for each row set kind.
 inline int64_t src_rows(const GemmParams& p, int set) {
-  if (set == SET_ROUTED) return p.gather ? (int64_t)p.sentinel / (p.topk > 0 ? p.topk : 1) : (int64_t)p.nsets * p.block;
+  if (set == SET_ROUTED)
+    return p.gather ? (int64_t)p.sentinel / (p.topk > 0 ? p.topk : 1) : (int64_t)p.nsets * p.block;
   if (set == SET_MASKED) return (int64_t)p.E * p.max_m;
   return (int64_t)p.nsets * p.block_rows;
 }

@@ -82,7 +82,9 @@ __device__ __forceinline__ void stage_barrier() {
 // stage_row(wave, 0, l) and stage_row(wave, 1, l); its piece i goes to stage
 // slot (4*wave + i)*64 + l: block 2*wave + i/2, quarter q = (2i + l/32) % 4,
 // row r = (l/2) % 16, position l % 2 holding step j = (l % 2) ^ (r / 8 % 2).
-__device__ __forceinline__ int stage_row(int wave, int i, int lane) { return 32 * wave + 16 * i + ((lane >> 1) & 15); }
+__device__ __forceinline__ int stage_row(int wave, int i, int lane) {
+  return 32 * wave + 16 * i + ((lane >> 1) & 15);
+}
 
 // The lane's copy sources: one base for the workgroup (the token matrix)
 // and the lane's two 32-bit byte offsets from it, its rows (at k = 0)
