@@ -150,6 +150,7 @@ CONTIG_CASES = [
     (8, 256, 128, 100, 4, 0, True),
     (8, 256, 128, 100, 4, 2, True),
     (12, 160, 96, 150, 3, 1, False),
+    (12, 160, 96, 150, 3, 1, True),        # H = 160: weighted rows padded to 192 features
     (4, 256, 128, 300, 2, 0, True),        # several 128-row blocks per expert
 ]
 

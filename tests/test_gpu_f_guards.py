@@ -41,6 +41,7 @@ def with_nan_row(bits):
 
 @pytest.mark.parametrize("E,H,I,T,topk,ovr", [
     (16, 256, 128, 37, 4, None),                 # small-M
+    (16, 160, 96, 37, 4, None),                  # H = 160: weighted rows padded to 192 features
     (8, 256, 256, 400, 4, None),                 # large-M (200 rows / expert)
     (16, 256, 128, 37, 4, {"dispatch": 2}),      # persistent job queue
 ])

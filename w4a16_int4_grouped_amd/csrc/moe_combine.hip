@@ -26,29 +26,32 @@ __device__ __forceinline__ f32x4_t keep_if(f32x4_t y, bool v) {
   return r;
 }
 
-// One thread per (token, 4 consecutive features). A row f is summed when
-// valid[f] >= 0 (the slot of f in the indexed layout's routing; 0 for the
-// contiguous layout's rows). With a routing header that does not describe
-// (E, block, T*topk) nothing was computed and the result is zero, as for the
-// GEMMs. A token's rows are loaded kRowBatch at a time before any is added,
-// so a thread keeps up to 8 rows' loads in flight instead of one. Rows still
-// add in ascending j; a skipped row (another GPU's expert) costs no read and
-// adds nothing (the sum starts at +0 and never becomes -0, so adding +0 is
-// exact).
+// One thread per (token, 8 adjacent positions of a row: two groups of 4 in
+// the W2 epilogue's lane-contiguous order, store_y24), read with one 16-byte
+// and one 8-byte load per row. A row f is summed when valid[f] >= 0 (the slot
+// of f in the indexed layout's routing; 0 for the contiguous layout's rows).
+// With a routing header that does not describe (E, block, T*topk) nothing was
+// computed and the result is zero, as for the GEMMs. A token's rows are loaded
+// kRowBatch at a time before any is added, so a thread keeps up to 8 rows'
+// loads in flight instead of one. Rows still add in ascending j; a skipped row
+// (another GPU's expert) costs no read and adds nothing (the sum starts at +0
+// and never becomes -0, so adding +0 is exact).
 constexpr int kRowBatch = 8;
 
 __global__ __launch_bounds__(256) void combine_rows(const uint16_t* __restrict__ yhi,
                                                     const uint8_t* __restrict__ ylo,
                                                     const int32_t* __restrict__ valid,
                                                     const int32_t* __restrict__ hdr, int E, int block,
-                                                    int T, int topk, int H4, int ld,
-                                                    u32x2_t* __restrict__ out) {
+                                                    int T, int topk, int H, int ld,
+                                                    uint16_t* __restrict__ out) {
   const int t = blockIdx.y;
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (t >= T || c >= H4) return;
+  const int p0 = 8 * (blockIdx.x * 256 + threadIdx.x);   // positions p0 .. p0 + 7 of the row
+  // position 16q + 4mt + i of a 64-feature block holds feature 16mt + 4q + i
+  const int blk = p0 & ~63, q = (p0 >> 4) & 3, mt0 = (p0 >> 2) & 3;   // mt0 is 0 or 2
+  if (t >= T || blk >= H) return;
   const bool ok = !hdr || (hdr[HDR_MAGIC] == kRoutingMagic && hdr[HDR_BLOCK] == block &&
                            hdr[HDR_E] == E && hdr[HDR_T] * hdr[HDR_TOPK] == T * topk);
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[2] = {};
   if (ok) {
     const int f0 = t * topk;
     for (int j0 = 0; j0 < topk; j0 += kRowBatch) {
@@ -56,20 +59,35 @@ __global__ __launch_bounds__(256) void combine_rows(const uint16_t* __restrict__
       bool use[kRowBatch];
 #pragma unroll
       for (int u = 0; u < kRowBatch; ++u) use[u] = j0 + u < topk && valid[f0 + j0 + u] >= 0;
-      f32x4_t y[kRowBatch];
+      u32x4_t h[kRowBatch];
+      u32x2_t l[kRowBatch];
 #pragma unroll
       for (int u = 0; u < kRowBatch; ++u) {
-        y[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (use[u]) y[u] = load_y24(yhi, ylo, (size_t)(f0 + j0 + u) * ld, 4 * c);
+        h[u] = u32x4_t{0u, 0u, 0u, 0u};   // +0 in every value
+        l[u] = u32x2_t{0u, 0u};
+        if (use[u]) {
+          const size_t idx = (size_t)(f0 + j0 + u) * ld + p0;
+          h[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(yhi + idx));
+          l[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(ylo + idx));
+        }
       }
 #pragma unroll
-      for (int u = 0; u < kRowBatch; ++u) acc += y[u];
+      for (int u = 0; u < kRowBatch; ++u) {
+        acc[0] += unpack_y24(h[u][0], h[u][1], l[u][0]);
+        acc[1] += unpack_y24(h[u][2], h[u][3], l[u][1]);
+      }
     }
   }
-  u32x2_t r;
-  r[0] = pack_bf16x2(acc[0], acc[1]);
-  r[1] = pack_bf16x2(acc[2], acc[3]);
-  out[(size_t)t * H4 + c] = r;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int n = blk + (mt0 + g) * 16 + q * 4;
+    if (n < H) {
+      u32x2_t r;
+      r[0] = pack_bf16x2(acc[g][0], acc[g][1]);
+      r[1] = pack_bf16x2(acc[g][2], acc[g][3]);
+      *reinterpret_cast<u32x2_t*>(out + (size_t)t * H + n) = r;
+    }
+  }
 }
 
 // Split-K reduction of W13 fused with its SwiGLU: one thread per (routing
@@ -222,10 +240,10 @@ hipError_t launch_combine_rows(const uint16_t* yhi, const uint8_t* ylo, int ld, 
                                const int32_t* hdr, int E, int block, int T, int topk, int H, uint16_t* out,
                                hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (ld % 64 || ld < H) return hipErrorInvalidValue;   // rows in 64-feature blocks (y24_pos)
-  const int H4 = H / 4;
-  hipLaunchKernelGGL(combine_rows, dim3((H4 + 255) / 256, T), dim3(256), 0, s, yhi, ylo, valid, hdr, E, block,
-                     T, topk, H4, ld, reinterpret_cast<u32x2_t*>(out));
+  if (ld % 64 || ld < H || H % 4) return hipErrorInvalidValue;   // rows in 64-feature blocks (store_y24)
+  const int pieces = (H + 63) / 64 * 8;   // 8-position pieces of a token's row blocks
+  hipLaunchKernelGGL(combine_rows, dim3((pieces + 255) / 256, T), dim3(256), 0, s, yhi, ylo, valid, hdr, E,
+                     block, T, topk, H, ld, out);
   return hipGetLastError();
 }
 

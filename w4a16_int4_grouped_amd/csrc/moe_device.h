@@ -197,9 +197,6 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 // them with full 16-byte stores and the 4 lanes of a row fill 128 bytes of
 // the high plane (with plain [n] order each lane would write 8- and 4-byte
 // pieces 32 bytes apart, which measured 40 % slower on the TP8 shard's W2).
-__device__ __forceinline__ int y24_pos(int n) {
-  return (n & ~63) | (((n >> 2) & 3) << 4) | (((n >> 4) & 3) << 2) | (n & 3);
-}
 
 // Stores G groups of 4 values (tiles mt0 .. mt0 + G - 1 of lane q) at row
 // element idx = block + 16*q + 4*mt0 (G = 4: mt0 = 0; G = 2: mt0 even).
@@ -226,18 +223,14 @@ __device__ __forceinline__ void store_y24(uint16_t* __restrict__ hi, uint8_t* __
     *reinterpret_cast<u32x2_t*>(lo + idx) = u32x2_t{l[0], l[1]};
 }
 
-// Features n0 .. n0 + 3 (n0 a multiple of 4) of a row stored by store_y24
-// (row element offset row0), as FP32.
-__device__ __forceinline__ f32x4_t load_y24(const uint16_t* __restrict__ hi, const uint8_t* __restrict__ lo,
-                                            size_t row0, int n0) {
-  const size_t idx = row0 + y24_pos(n0);
-  const u32x2_t h = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(hi + idx));
-  const uint32_t l = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(lo + idx));
+// One group of 4 values stored by store_y24 (high-plane dwords ha, hb and
+// low-plane dword l), as FP32.
+__device__ __forceinline__ f32x4_t unpack_y24(uint32_t ha, uint32_t hb, uint32_t l) {
   f32x4_t v;
-  v[0] = __uint_as_float((h[0] << 16) | ((l & 0xFFu) << 8));
-  v[1] = __uint_as_float((h[0] & 0xFFFF0000u) | (l & 0xFF00u));
-  v[2] = __uint_as_float((h[1] << 16) | ((l >> 8) & 0xFF00u));
-  v[3] = __uint_as_float((h[1] & 0xFFFF0000u) | ((l >> 16) & 0xFF00u));
+  v[0] = __uint_as_float((ha << 16) | ((l & 0xFFu) << 8));
+  v[1] = __uint_as_float((ha & 0xFFFF0000u) | (l & 0xFF00u));
+  v[2] = __uint_as_float((hb << 16) | ((l >> 8) & 0xFF00u));
+  v[3] = __uint_as_float((hb & 0xFFFF0000u) | ((l >> 16) & 0xFF00u));
   return v;
 }
 

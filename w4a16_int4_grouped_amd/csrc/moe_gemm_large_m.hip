@@ -212,7 +212,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c, 
       }
       if (f < 0 || f >= p.sentinel) continue;
       const float w = p.topk_w[f];
-      if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (y24_pos)
+      if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (store_y24)
         f32x4_t v[kMT];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) v[mt] = w * acc[mt][nt];
@@ -287,7 +287,7 @@ __device__ __forceinline__ void epilogue_meta(const GemmParams& p, const TileCtx
       }
     } else if constexpr (EPI == EPI_COMBINE) {
       const float w = m.w[r];
-      if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (y24_pos)
+      if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (store_y24)
         f32x4_t v[kMT];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) v[mt] = w * acc[mt][nt];

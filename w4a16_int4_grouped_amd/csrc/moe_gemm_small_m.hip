@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
         }
         if (f < 0 || f >= p.sentinel) continue;
         const float w = p.topk_w[f];
-        if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (y24_pos)
+        if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (store_y24)
           f32x4_t v[kMT];
 #pragma unroll
           for (int mt = 0; mt < kMT; ++mt) v[mt] = w * acc[mt][nt];
@@ -539,7 +539,7 @@ __device__ __forceinline__ void job_epilogue(const GemmParams& p, const f32x4_t 
       }
     } else if constexpr (EPI == EPI_COMBINE) {
       const float w = p.topk_w[f];
-      if (b.rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (y24_pos)
+      if (b.rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (store_y24)
         f32x4_t v[kMT];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) v[mt] = w * acc[mt][nt];
