@@ -6,6 +6,6 @@ CPU-baseline leg of ``bench.py`` may import this package. The product path
 """
 from .moe_oracle import (  # noqa: F401
     bf16_round, bf16_to_f64, unpack_nibbles, dequant, align, permute,
-    contiguous_layout, silu, expert_ffn, moe_indexed, moe_contiguous, moe_masked,
+    contiguous_layout, silu, expert_ffn, combine, moe_indexed, moe_contiguous, moe_masked,
     compare,
 )

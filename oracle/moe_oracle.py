@@ -16,9 +16,10 @@ other rounding is the BF16 intermediate ``a`` (the second GEMM's BF16 input).
 The reference output stays unrounded (float64).
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
-(library special cases, closed forms, brute force, invariants). The full-size
-layer outputs are trusted through those pins; the pages print no worked
-numerical example of the layer.
+(library special cases, closed forms, brute force, invariants, hand-worked
+fixtures under tests/golden/, including the comparison metrics and the
+permutation). The full-size layer outputs are trusted through those pins; the
+pages print no worked numerical example of the layer.
 """
 from __future__ import annotations
 
@@ -167,7 +168,9 @@ def permute(x_bits, al: dict, topk: int) -> np.ndarray:
     """Gather activation rows into the sorted, padded order of an alignment.
 
     Row p of the result is x[sorted_ids[p] // topk] for a routed slot and a
-    zero row for a sentinel slot; there are cap rows.
+    zero row for a sentinel slot; there are cap rows. This is the gather the
+    indexed layout leaves to the kernel: unpadded activations, padding carried
+    by sentinel indices (Chord page, "Grouped SM90 kernels", Fig. 3).
     """
     x = np.asarray(x_bits)
     sid = al["sorted_ids"].astype(np.int64)
@@ -308,11 +311,24 @@ def moe_indexed(x_bits, topk_ids, topk_w, weights, E: int, tokens=None, keep=Fal
             for r, (ti, j) in enumerate(sel):
                 f = int(tok[ti]) * k + int(j)
                 rows_h[f], rows_a[f], rows_y[f] = h[r], a[r], y[r]
-    out = np.zeros((tok.size, H), dtype=np.float64)
-    for j in range(k):
-        out += w[tok, j][:, None] * Y[:, j]
+    out = combine(Y, w[tok])
     if keep:
         return out, dict(h=rows_h, a=rows_a, y=rows_y)
+    return out
+
+
+def combine(Y, topk_w) -> np.ndarray:
+    """Top-k-weighted combine: out[t] = sum_j topk_w[t, j] * Y[t, j], the
+    terms added in ascending j in float64 and left unrounded. Y is
+    [T, topk, H] (zero for a row routed nowhere), topk_w is [T, topk].
+    Reading: the routing weight multiplies the second GEMM's output (the
+    north-star statement's "top-k-weighted combine"; the Chord page's timings
+    exclude it, "Measurements")."""
+    Y = np.asarray(Y, dtype=np.float64)
+    w = np.asarray(topk_w).astype(np.float64)
+    out = np.zeros((Y.shape[0], Y.shape[2]), dtype=np.float64)
+    for j in range(Y.shape[1]):
+        out += w[:, j][:, None] * Y[:, j]
     return out
 
 
@@ -349,9 +365,7 @@ def moe_contiguous(a_bits, m_indices, weights, row_src=None, topk_w=None, T=None
     ok = (src >= 0) & (m_idx >= 0)
     f = src[ok].astype(np.int64)
     Y[f // topk, f % topk] = y_all[ok]
-    out = np.zeros((T, H))
-    for j in range(topk):
-        out += w[:, j][:, None] * Y[:, j]
+    out = combine(Y, w)
     return (out, a_rows) if keep else out
 
 

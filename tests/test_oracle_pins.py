@@ -574,6 +574,41 @@ def test_compare_metrics():
     assert abs(m["rms"] - math.sqrt(12.5)) < 1e-12
 
 
+def pin_compare_golden():
+    """The comparison's four figures on hand-worked 4-element cases
+    (tests/golden/compare_cases.txt derives each one)."""
+    for row in _read_rows("compare_cases.txt"):
+        ref = np.array([float.fromhex(v) for v in row[1:5]])
+        got = np.array([float.fromhex(v) for v in row[5:9]])
+        rms, rel, mx, floor = (float(v) for v in row[9:13])
+        m = O.compare(got, ref)
+        for key, want in (("rms", rms), ("rel_fro", rel), ("max_abs_over_rms", mx), ("bf16_floor", floor)):
+            assert abs(m[key] - want) <= 1e-15 + 1e-13 * abs(want), (row[0], key, m[key], want)
+        assert m["n"] == 4
+
+
+def test_compare_golden():
+    pin_compare_golden()
+
+
+def pin_permute_golden():
+    """Gather into the aligned order, sentinel slots zero
+    (tests/golden/permute_cases.txt derives the rows by hand)."""
+    rows = _read_rows("permute_cases.txt")
+    T, H, k, E, B = (int(v) for v in rows[0])
+    x = np.array([[int(v, 16) for v in r] for r in rows[1:1 + T]], dtype=np.uint16)
+    ids = np.array([[int(v) for v in r] for r in rows[1 + T:1 + 2 * T]], dtype=np.int32)
+    want = np.array([[int(v, 16) for v in r] for r in rows[1 + 2 * T:]], dtype=np.uint16)
+    al = O.align(ids, E, B)
+    assert al["cap"] == want.shape[0]
+    got = O.permute(x, al, k)
+    assert got.dtype == np.uint16 and np.array_equal(got, want), got
+
+
+def test_permute_golden():
+    pin_permute_golden()
+
+
 # --------------------------------------------------------------------------
 # Planted mistakes: each must make at least one pin fail
 # --------------------------------------------------------------------------
@@ -646,10 +681,89 @@ def _gate_up_truncated(x_rows_bits, w13_bits):
     return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
+def _compare_floor_doubled(got, ref):
+    m = COMPARE_ORIG(got, ref)
+    m["bf16_floor"] *= 2
+    return m
+
+
+def _compare_max_abs_halved(got, ref):
+    m = COMPARE_ORIG(got, ref)
+    m["max_abs_over_rms"] *= 0.5
+    return m
+
+
+def _compare_rel_fro_over_got(got, ref):
+    m = COMPARE_ORIG(got, ref)
+    g, r = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    m["rel_fro"] = float(np.linalg.norm(g - r) / np.linalg.norm(g))
+    return m
+
+
+def _compare_floor_truncated(got, ref):
+    m = COMPARE_ORIG(got, ref)
+    r = np.asarray(ref, dtype=np.float64)
+    t = ((r.astype(np.float32).view(np.uint32) >> 16) << 16).view(np.float32).astype(np.float64)
+    m["bf16_floor"] = float(np.max(np.abs(t - r))) / m["rms"]
+    return m
+
+
+def _compare_floor_over_max(got, ref):
+    m = COMPARE_ORIG(got, ref)
+    r = np.asarray(ref, dtype=np.float64)
+    m["bf16_floor"] = m["bf16_floor"] * m["rms"] / float(np.max(np.abs(r)))
+    return m
+
+
+def _compare_floor_of_got(got, ref):
+    m = COMPARE_ORIG(got, ref)
+    g = np.asarray(got, dtype=np.float64)
+    m["bf16_floor"] = float(np.max(np.abs(O.bf16_to_f64(O.bf16_round(g)) - g))) / m["rms"]
+    return m
+
+
+def _compare_rms_of_sum(got, ref):
+    m = COMPARE_ORIG(got, ref)
+    r = np.asarray(ref, dtype=np.float64)
+    rms2 = float(np.sqrt(np.sum(r * r)))
+    m["max_abs_over_rms"] *= m["rms"] / rms2
+    m["bf16_floor"] *= m["rms"] / rms2
+    m["rms"] = rms2
+    return m
+
+
+def _permute_mod_topk(x_bits, al, topk):
+    x = np.asarray(x_bits)
+    sid = al["sorted_ids"].astype(np.int64)
+    out = np.zeros((sid.size, x.shape[1]), dtype=np.uint16)
+    ok = sid < al["sentinel"]
+    out[ok] = x[sid[ok] % topk]
+    return out
+
+
+def _permute_pad_last_row(x_bits, al, topk):
+    out = PERMUTE_ORIG(x_bits, al, topk)
+    sid = al["sorted_ids"]
+    out[sid >= al["sentinel"]] = np.asarray(x_bits)[-1]
+    return out
+
+
+def _permute_off_by_one(x_bits, al, topk):
+    x = np.asarray(x_bits)
+    sid = al["sorted_ids"].astype(np.int64)
+    out = np.zeros((sid.size, x.shape[1]), dtype=np.uint16)
+    ok = sid < al["sentinel"]
+    out[ok] = x[np.minimum((sid[ok] + 1) // topk, x.shape[0] - 1)]
+    return out
+
+
 ALIGN_ORIG = O.align
+COMPARE_ORIG = O.compare
+PERMUTE_ORIG = O.permute
 PINS = [pin_bf16_vs_torch, pin_unpack_golden, pin_dequant_golden, pin_align_golden,
         pin_align_bruteforce, pin_layer_bruteforce, pin_layer_onehot, pin_split_identity,
-        pin_layout_equality, pin_unfused_onehot, pin_unfused_bruteforce, pin_ep_shards]
+        pin_layout_equality, pin_unfused_onehot, pin_unfused_bruteforce, pin_ep_shards,
+        pin_compare_golden, pin_permute_golden]
 
 
 @pytest.mark.parametrize("name,attr,bad", [
@@ -662,6 +776,16 @@ PINS = [pin_bf16_vs_torch, pin_unpack_golden, pin_dequant_golden, pin_align_gold
     ("bf16 ties away from zero", "bf16_round", _round_ties_away),
     ("unfused SwiGLU halves swapped", "swiglu_rows", _swiglu_swapped),
     ("unfused gate_up unrounded h truncated", "gate_up_rows", _gate_up_truncated),
+    ("compare: BF16 floor doubled", "compare", _compare_floor_doubled),
+    ("compare: max-abs halved", "compare", _compare_max_abs_halved),
+    ("compare: rel_fro over ||got||", "compare", _compare_rel_fro_over_got),
+    ("compare: floor by truncation", "compare", _compare_floor_truncated),
+    ("compare: floor over max|ref|", "compare", _compare_floor_over_max),
+    ("compare: floor of got", "compare", _compare_floor_of_got),
+    ("compare: rms as sqrt(sum)", "compare", _compare_rms_of_sum),
+    ("permute: token = flat % topk", "permute", _permute_mod_topk),
+    ("permute: pad slots copy a row", "permute", _permute_pad_last_row),
+    ("permute: flat index off by one", "permute", _permute_off_by_one),
 ])
 def test_planted_mistakes_are_caught(monkeypatch, name, attr, bad):
     monkeypatch.setattr(O, attr, bad)
