@@ -277,7 +277,14 @@ moe_status_t moe_permute(const moe_weights_t* h, const uint16_t* x, int32_t T, i
 size_t moe_workspace_bytes(const moe_weights_t* h, int32_t mode, int32_t rows, int32_t topk,
                            int32_t tokens, const moe_tuning_t* ovr);
 
-/* Indexed layout. Unpadded activations, routing by moe_align.
+/* Indexed layout (Chord page, "Grouped SM90 kernels", Fig. 3: activations
+ * stay unpadded and the padding lives in the routing indices as sentinels;
+ * "Indexed kernels" and "H200 and Blackwell indexed decode": the decode
+ * schedule follows rows per expert, and block_m / tuning overrides are
+ * accepted on this layout only). One call runs the whole layer: W13
+ * (gate | up) grouped GEMM with the uint4 dequantisation fused into the
+ * weight load, SwiGLU, the W2 grouped GEMM and the top-k-weighted combine
+ * out[t] = sum_j topk_w[t, j] * y(t, j).
  *   x        device bf16 [T, H]
  *   topk_ids device int32 [T, topk], topk_w device float [T, topk]
  *   routing  device buffer from moe_align(h, topk_ids, T, topk, ovr, ...) on

@@ -4,6 +4,7 @@
 // sequencing on the caller's stream, and optional per-kernel event timing.
 #include <hip/hip_runtime.h>
 
+#include <array>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -11,7 +12,6 @@
 #include <map>
 #include <mutex>
 #include <string>
-#include <unordered_map>
 #include <vector>
 
 #include "moe_launch.h"
@@ -246,6 +246,13 @@ int nt_for_rows(int rows) {
 
 }  // namespace
 
+// The memo key: the whole descriptor a schedule is a function of (mode, the
+// two shape ints, and every override field), compared field by field.
+struct ScheduleKey {
+  std::array<int32_t, 8> v;
+  bool operator<(const ScheduleKey& o) const { return v < o.v; }
+};
+
 struct moe_weights {
   moe_weight_desc_t desc{};
   PreparedLayout lay;
@@ -254,21 +261,15 @@ struct moe_weights {
   int device = 0;
   EnvOverrides env;
   std::mutex mu;
-  std::unordered_map<uint64_t, Schedule> cache;
+  std::map<ScheduleKey, Schedule> cache;
 };
 
 namespace {
 
-uint64_t key_of(int mode, int a, int b, const moe_tuning_t* o) {
-  uint64_t k = (uint64_t)(mode & 3);
-  k = k * 1000003u + (uint32_t)a;
-  k = k * 1000003u + (uint32_t)b;
-  if (o) {
-    k = k * 1000003u + (uint32_t)o->block_m;
-    k = k * 1000003u + (uint32_t)o->schedule;
-    k = k * 1000003u + (uint32_t)o->dispatch;
-    k = k * 1000003u + (uint32_t)o->global_experts;
-  }
+ScheduleKey key_of(int mode, int a, int b, const moe_tuning_t* o) {
+  ScheduleKey k{};
+  k.v = {mode, a, b, o != nullptr, o ? o->block_m : 0, o ? o->schedule : 0,
+         o ? o->dispatch : 0, o ? o->global_experts : 0};
   return k;
 }
 
@@ -292,7 +293,7 @@ bool large_m_rejected(const moe_weights* h, const moe_tuning_t* ovr) {
 // Chord page's tok_e rule: tokens per expert, not total tokens). Large-M
 // aligns each expert to 128-row blocks, its token tile.
 Schedule schedule_indexed(moe_weights* h, int T, int topk, const moe_tuning_t* ovr) {
-  const uint64_t key = key_of(MOE_MODE_INDEXED, T, topk, ovr);
+  const ScheduleKey key = key_of(MOE_MODE_INDEXED, T, topk, ovr);
   std::lock_guard<std::mutex> g(h->mu);
   auto it = h->cache.find(key);
   if (it != h->cache.end()) return it->second;
@@ -343,7 +344,7 @@ Schedule schedule_indexed(moe_weights* h, int T, int topk, const moe_tuning_t* o
 }
 
 Schedule schedule_masked(moe_weights* h, int max_m, int expected_m) {
-  const uint64_t key = key_of(MOE_MODE_MASKED, max_m, expected_m, nullptr);
+  const ScheduleKey key = key_of(MOE_MODE_MASKED, max_m, expected_m, nullptr);
   std::lock_guard<std::mutex> g(h->mu);
   auto it = h->cache.find(key);
   if (it != h->cache.end()) return it->second;
@@ -366,7 +367,7 @@ Schedule schedule_masked(moe_weights* h, int max_m, int expected_m) {
 // Contiguous: every block is a full 128-row tile, which the large-M kernel
 // covers in one weight pass.
 Schedule schedule_contiguous(moe_weights* h, int M_pad) {
-  const uint64_t key = key_of(MOE_MODE_CONTIGUOUS, M_pad, 0, nullptr);
+  const ScheduleKey key = key_of(MOE_MODE_CONTIGUOUS, M_pad, 0, nullptr);
   std::lock_guard<std::mutex> g(h->mu);
   auto it = h->cache.find(key);
   if (it != h->cache.end()) return it->second;
