@@ -1,10 +1,24 @@
 """Full-size parity: the workloads at their real shapes, run on the GPU
-exactly as the benchmark runs them, checked against the CPU oracle on
-sampled tokens / experts (the oracle recomputes those from the same seeded
-inputs). The contiguous result is compared with the oracle's indexed result
-for the same routing, which the layout-equality pin shows to be the same
-quantity."""
+exactly as the benchmark runs them, checked against the CPU oracle.
+
+Every expert that holds rows is compared at least once:
+  * indexed layouts (decode, TP8 shard, EP8 decode share): tokens are chosen
+    greedily until every routed expert appears among their top-k rows, and
+    those tokens' whole combined outputs are compared;
+  * masked: the first and the last valid row of every expert;
+  * contiguous prefill: the same greedy cover plus the last tokens routed to
+    the three most popular Zipf experts (their rows sit in those experts' last
+    128-row block), compared per token against the oracle's indexed result for
+    the same routing (the layout-equality pin shows it is the same quantity);
+  * EP8 prefill share (48 experts x 512 aligned rows): rows of every expert,
+    its last row included.
+The oracle's per-expert work (exact dequantisation, the two GEMMs in float64)
+is shared by the workloads that use the same weights and runs on a thread
+pool; this file only decides which rows to compute and where they go.
+"""
+import concurrent.futures as cf
 import gc
+import time
 
 import numpy as np
 import pytest
@@ -14,21 +28,86 @@ from oracle import moe_oracle as O
 from tests.gpu_util import (bf16_dev, bits_host, check_tol, f32_dev, i32_dev, log, prepare,
                             require_gpu, weights_dev)
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+
+ORACLE_THREADS = 16
 
 
-def _provider(w):
-    cache = {}
+def cover_tokens(ids, first=()):
+    """Tokens (ascending) such that every id >= 0 in ``ids`` [T, k] occurs in
+    one of their rows: ``first`` plus, greedily, the token adding the most
+    experts not yet covered."""
+    sets = [set(int(v) for v in r if v >= 0) for r in ids]
+    want = set().union(*sets)
+    chosen = list(dict.fromkeys(int(t) for t in first))
+    seen = set().union(*(sets[t] for t in chosen)) if chosen else set()
+    while seen != want:
+        t = max(range(len(sets)), key=lambda i: len(sets[i] - seen))
+        chosen.append(t)
+        seen |= sets[t]
+    return np.array(sorted(chosen))
 
-    def get(e):
-        if e not in cache:
-            cache[e] = (w[0][e], w[1][e], w[2][e], w[3][e])
-        return cache[e]
-    return get
+
+class RowRequests:
+    """Rows to run through the oracle, grouped by expert. add() returns a
+    handle; result(handle) gives the oracle's float64 y rows after run()."""
+
+    def __init__(self):
+        self.rows = {}        # expert -> list of x row arrays
+        self.out = {}
+
+    def add(self, e, x_rows):
+        lst = self.rows.setdefault(int(e), [])
+        start = sum(len(r) for r in lst)
+        lst.append(np.asarray(x_rows))
+        return int(e), start, len(x_rows)
+
+    def run(self, weights, what):
+        """weights: (w13_q, w13_s, w2_q, w2_s) stacked over experts."""
+        t0 = time.time()
+        experts = sorted(self.rows)
+
+        def one(e):
+            x = np.concatenate(self.rows[e])
+            w13 = O.dequant(weights[0][e], weights[1][e])
+            w2 = O.dequant(weights[2][e], weights[3][e])
+            return e, O.expert_ffn(x, w13, w2)[2]
+        with cf.ThreadPoolExecutor(ORACLE_THREADS) as ex:
+            for i, (e, y) in enumerate(ex.map(one, experts)):
+                self.out[e] = y
+                if (i + 1) % 96 == 0:
+                    log(f"  oracle {what}: {i + 1}/{len(experts)} experts, {time.time() - t0:.0f} s")
+        log(f"  oracle {what}: {len(experts)} experts, "
+            f"{sum(len(v) for v in self.out.values())} rows in {time.time() - t0:.0f} s")
+
+    def result(self, handle):
+        e, start, n = handle
+        return self.out[e][start:start + n]
+
+
+def indexed_request(req, x, ids, tokens):
+    """Queue the (token, j) rows of ``tokens``; returns the placement."""
+    place = []
+    for ti, t in enumerate(tokens):
+        for j in range(ids.shape[1]):
+            if ids[t, j] >= 0:
+                place.append((ti, j, req.add(ids[t, j], x[t:t + 1])))
+    return place
+
+
+def indexed_reference(req, place, tw, tokens, H):
+    """The oracle's combine of the queued rows: [len(tokens), H] float64."""
+    Y = np.zeros((len(tokens), tw.shape[1], H))
+    for ti, j, hd in place:
+        Y[ti, j] = req.result(hd)[0]
+    return O.combine(Y, tw[tokens])
 
 
 @pytest.fixture(scope="module")
 def kimi():
+    """Decode, masked, prefill and the two EP8 shares on the 384-expert
+    H=7168 I=2048 weights, run on the GPU; then one oracle pass over every
+    expert for all of them."""
     require_gpu()
     import torch
     wl = synth.WORKLOADS[1]
@@ -36,127 +115,148 @@ def kimi():
     w = synth.stacked_weights(wl)
     dw = weights_dev(*w)
     torch.cuda.synchronize()
-    yield wl, w, dw
-    del dw
-    gc.collect()
-    torch.cuda.empty_cache()
+    req = RowRequests()
+    res = {}
 
-
-def test_full_decode_indexed(kimi):
-    import torch
-    wl, w, dw = kimi
+    # decode, indexed
     log(f"case {wl.name}")
     h = prepare(None, "indexed", dev_weights=dw)
     x = synth.activations(wl.iseed, wl.T, wl.H)
     ids, tw = synth.routing(wl)
-    out = bits_host(h.indexed(bf16_dev(x), i32_dev(ids), f32_dev(tw)))
+    out = O.bf16_to_f64(bits_host(h.indexed(bf16_dev(x), i32_dev(ids), f32_dev(tw))))
     torch.cuda.synchronize()
-    outf = O.bf16_to_f64(out)
-    assert np.all(np.isfinite(outf))
-    assert np.all(np.abs(outf).sum(axis=1) > 0)
-    sample = np.array([0, wl.T - 1])
-    ref = O.moe_indexed(x, ids, tw, _provider(w), E=wl.E, tokens=sample)
-    check_tol(outf[sample], ref, f"{wl.name} tokens {sample.tolist()}")
+    tok = cover_tokens(ids)
+    res["decode"] = dict(out=out, tok=tok, tw=tw, place=indexed_request(req, x, ids, tok))
     del h
+
+    # masked
+    wlm = synth.WORKLOADS[3]
+    log(f"case {wlm.name}")
+    h = prepare(None, "masked", dev_weights=dw)
+    a3, mm = synth.masked_inputs(wlm)
+    outm = h.masked(bf16_dev(a3), i32_dev(mm), wlm.expected_m)
+    torch.cuda.synchronize()
+    rows, place = [], []
+    for e in range(wlm.E):
+        m = int(mm[e])
+        for r in sorted({0, m - 1}) if m > 0 else ():
+            rows.append(e * wlm.max_m + r)
+            place.append(req.add(e, a3[e, r:r + 1]))
+    got = O.bf16_to_f64(bits_host(outm[torch.from_numpy(np.array(rows)).cuda()]))
+    res["masked"] = dict(got=got, place=place, experts=int(np.count_nonzero(mm)))
+    del h, outm
+
+    # prefill, contiguous with the per-token combine
+    wlp = synth.WORKLOADS[2]
+    log(f"case {wlp.name}")
+    h = prepare(None, "contiguous", dev_weights=dw)
+    xp = synth.activations(wlp.iseed, wlp.T, wlp.H)
+    idp, twp = synth.routing(wlp)
+    a, m_idx, row_src = O.contiguous_layout(xp, idp, wlp.E, 128)
+    log(f"  M_pad={a.shape[0]} (valid rows {int((m_idx >= 0).sum())})")
+    outp = O.bf16_to_f64(bits_host(h.contiguous(bf16_dev(a), i32_dev(m_idx), i32_dev(row_src),
+                                                f32_dev(twp), wlp.T, wlp.topk)))
+    torch.cuda.synchronize()
+    counts = np.bincount(idp.reshape(-1), minlength=wlp.E)
+    hot = np.argsort(-counts, kind="stable")[:3]
+    last = [t for e in hot for t in np.flatnonzero(np.any(idp == e, axis=1))[-4:]]
+    tokp = cover_tokens(idp, first=[0, wlp.T - 1, *last])
+    log(f"  hottest experts {hot.tolist()} with {counts[hot].tolist()} rows; {len(tokp)} tokens")
+    res["prefill"] = dict(out=outp, tok=tokp, tw=twp, place=indexed_request(req, xp, idp, tokp),
+                          hot_tokens=last)
+    del h, a
+
+    # EP8 decode share: experts 0..47 of the 384, global ids through the map
+    wle = synth.WORKLOADS[5]
+    Eg = wle.extra["global_experts"]
+    log(f"case {wle.name}")
+    ws = tuple(v[:wle.E] for v in w)
+    h = prepare(ws, "indexed")
+    xe = synth.activations(wle.iseed, wle.T, wle.H)
+    ide, twe = synth.routing(wle)
+    emap = np.full(Eg, -1, dtype=np.int32)
+    emap[:wle.E] = np.arange(wle.E)
+    ovr = {"global_experts": Eg}
+    log(f"  {h.describe(wle.T, wle.topk, ovr=ovr)}")
+    routing = h.align_ep(i32_dev(ide), i32_dev(emap), Eg, ovr=ovr)
+    oute = O.bf16_to_f64(bits_host(h.indexed(bf16_dev(xe), i32_dev(ide), f32_dev(twe),
+                                             routing=routing, ovr=ovr)))
+    torch.cuda.synchronize()
+    loc = O.ep_local_ids(ide, emap)      # local id == global id for this share
+    toke = cover_tokens(loc)
+    res["ep_decode"] = dict(out=oute, tok=toke, tw=twe, place=indexed_request(req, xe, loc, toke),
+                            none=np.flatnonzero(np.all(loc < 0, axis=1)))
+    del h, routing
+
+    # EP8 prefill share: 48 experts x 512 aligned rows, no combine
+    wlg = synth.WORKLOADS[6]
+    rpe = wlg.extra["rows_per_expert"]
+    log(f"case {wlg.name}")
+    h = prepare(ws, "contiguous")
+    ag = synth.activations(wlg.iseed, wlg.E * rpe, wlg.H)
+    mg = np.repeat(np.arange(wlg.E, dtype=np.int32), rpe)
+    log(f"  {h.describe(wlg.E * rpe)}")
+    outg = h.contiguous(bf16_dev(ag), i32_dev(mg))
+    torch.cuda.synchronize()
+    rows, place = [], []
+    for e in range(wlg.E):
+        sel = np.unique(np.r_[e * rpe + np.arange(0, rpe, 97) + e % 7, e * rpe + rpe - 1])
+        rows.extend(sel.tolist())
+        place.append(req.add(e, ag[sel]))
+    got = O.bf16_to_f64(bits_host(outg[torch.from_numpy(np.array(rows)).cuda()]))
+    res["ep_prefill"] = dict(got=got, place=place)
+    del h, outg
+
+    del dw
+    gc.collect()
+    torch.cuda.empty_cache()
+    req.run(w, "384 experts, H=7168 I=2048")
+    yield req, res
+
+
+def test_full_decode_indexed(kimi):
+    req, res = kimi
+    r = res["decode"]
+    wl = synth.WORKLOADS[1]
+    assert np.all(np.isfinite(r["out"]))
+    assert np.all(np.abs(r["out"]).sum(axis=1) > 0)
+    ref = indexed_reference(req, r["place"], r["tw"], r["tok"], wl.H)
+    check_tol(r["out"][r["tok"]], ref, f"{wl.name}: {len(r['tok'])} tokens covering every expert")
 
 
 def test_full_masked(kimi):
-    import torch
-    _, w, dw = kimi
-    wl = synth.WORKLOADS[3]
-    log(f"case {wl.name}")
-    h = prepare(None, "masked", dev_weights=dw)
-    a3, mm = synth.masked_inputs(wl)
-    out = h.masked(bf16_dev(a3), i32_dev(mm), wl.expected_m)
-    torch.cuda.synchronize()
-    experts = [0, int(np.argmax(mm)), 200, wl.E - 1]
-    experts = [e for e in dict.fromkeys(experts) if mm[e] > 0]
-    prov = _provider(w)
-    ref = O.moe_masked(a3[experts], mm[experts], lambda i: prov(experts[i]))
-    rows_ref, rows_got = [], []
-    for i, e in enumerate(experts):
-        rows_ref.append(ref[i * wl.max_m:i * wl.max_m + mm[e]])
-        rows_got.append(np.arange(e * wl.max_m, e * wl.max_m + mm[e]))
-    got = O.bf16_to_f64(bits_host(out[torch.from_numpy(np.concatenate(rows_got)).cuda()]))
-    check_tol(got, np.concatenate(rows_ref), f"{wl.name} experts {experts}")
-    del h
+    req, res = kimi
+    r = res["masked"]
+    ref = np.concatenate([req.result(hd) for hd in r["place"]])
+    check_tol(r["got"], ref, f"masked: first and last valid row of all {r['experts']} experts with rows")
 
 
 def test_full_prefill_contiguous(kimi):
-    import torch
-    _, w, dw = kimi
+    req, res = kimi
+    r = res["prefill"]
     wl = synth.WORKLOADS[2]
-    log(f"case {wl.name}")
-    h = prepare(None, "contiguous", dev_weights=dw)
-    x = synth.activations(wl.iseed, wl.T, wl.H)
-    ids, tw = synth.routing(wl)
-    a, m_idx, row_src = O.contiguous_layout(x, ids, wl.E, 128)
-    log(f"  M_pad={a.shape[0]} (valid rows {int((m_idx >= 0).sum())})")
-    out = h.contiguous(bf16_dev(a), i32_dev(m_idx), i32_dev(row_src), f32_dev(tw), wl.T, wl.topk)
-    torch.cuda.synchronize()
-    outf = O.bf16_to_f64(bits_host(out))
-    assert np.all(np.isfinite(outf))
-    sample = np.array([0, wl.T - 1])
-    ref = O.moe_indexed(x, ids, tw, _provider(w), E=wl.E, tokens=sample)
-    check_tol(outf[sample], ref, f"{wl.name} tokens {sample.tolist()}")
-    del h
+    assert np.all(np.isfinite(r["out"]))
+    assert len(r["tok"]) >= 64
+    ref = indexed_reference(req, r["place"], r["tw"], r["tok"], wl.H)
+    check_tol(r["out"][r["tok"]], ref, f"{wl.name}: {len(r['tok'])} tokens covering every expert")
+    hot = np.isin(r["tok"], r["hot_tokens"])
+    check_tol(r["out"][r["tok"][hot]], ref[hot], "prefill: last tokens of the three hottest experts")
 
 
 def test_full_ep8_share_decode(kimi):
-    """One GPU's EP8 share of the decode workload: experts 0..47 of the 384
-    (the same weights), global ids through the share's map."""
-    import torch
-    _, w, _ = kimi
+    req, res = kimi
+    r = res["ep_decode"]
     wl = synth.WORKLOADS[5]
-    Eg = wl.extra["global_experts"]
-    log(f"case {wl.name}")
-    ws = tuple(a[:wl.E] for a in w)
-    h = prepare(ws, "indexed")
-    x = synth.activations(wl.iseed, wl.T, wl.H)
-    ids, tw = synth.routing(wl)
-    emap = np.full(Eg, -1, dtype=np.int32)
-    emap[:wl.E] = np.arange(wl.E)
-    ovr = {"global_experts": Eg}
-    log(f"  {h.describe(wl.T, wl.topk, ovr=ovr)}")
-    routing = h.align_ep(i32_dev(ids), i32_dev(emap), Eg, ovr=ovr)
-    out = O.bf16_to_f64(bits_host(h.indexed(bf16_dev(x), i32_dev(ids), f32_dev(tw), routing=routing,
-                                            ovr=ovr)))
-    torch.cuda.synchronize()
-    loc = O.ep_local_ids(ids, emap)
-    has = np.flatnonzero(np.any(loc >= 0, axis=1))
-    none = np.flatnonzero(np.all(loc < 0, axis=1))
-    assert np.all(out[none] == 0)
-    sample = np.array([has[0], has[len(has) // 2], has[-1]])
-    ref = O.moe_indexed(x, loc, tw, _provider(ws), E=wl.E, tokens=sample)
-    check_tol(out[sample], ref, f"{wl.name} tokens {sample.tolist()}")
-    del h
+    assert np.all(r["out"][r["none"]] == 0)
+    ref = indexed_reference(req, r["place"], r["tw"], r["tok"], wl.H)
+    check_tol(r["out"][r["tok"]], ref, f"{wl.name}: {len(r['tok'])} tokens covering the 48 experts")
 
 
 def test_full_ep8_share_prefill_grouped(kimi):
-    """One GPU's EP8 share at prefill: 48 experts x 512 aligned grouped rows
-    (contiguous layout, no combine), checked on sampled experts' rows."""
-    import torch
-    _, w, _ = kimi
-    wl = synth.WORKLOADS[6]
-    rpe = wl.extra["rows_per_expert"]
-    log(f"case {wl.name}")
-    ws = tuple(a[:wl.E] for a in w)
-    h = prepare(ws, "contiguous")
-    total = wl.E * rpe
-    a = synth.activations(wl.iseed, total, wl.H)
-    m_idx = np.repeat(np.arange(wl.E, dtype=np.int32), rpe)
-    log(f"  {h.describe(total)}")
-    out = h.contiguous(bf16_dev(a), i32_dev(m_idx))
-    torch.cuda.synchronize()
-    prov = _provider(ws)
-    for e in (0, wl.E - 1):
-        rows = np.arange(e * rpe, e * rpe + rpe)[::37]
-        w13 = O.dequant(*prov(e)[:2])
-        w2 = O.dequant(*prov(e)[2:])
-        _, _, y = O.expert_ffn(a[rows], w13, w2)
-        got = O.bf16_to_f64(bits_host(out[torch.from_numpy(rows).cuda()]))
-        check_tol(got, y, f"{wl.name} expert {e} rows {rows[:3].tolist()}..")
-    del h
+    req, res = kimi
+    r = res["ep_prefill"]
+    ref = np.concatenate([req.result(hd) for hd in r["place"]])
+    check_tol(r["got"], ref, f"EP8 prefill share: {len(ref)} rows over all 48 experts")
 
 
 def test_full_tp8_shard_indexed():
@@ -170,10 +270,14 @@ def test_full_tp8_shard_indexed():
     ids, tw = synth.routing(wl)
     out = O.bf16_to_f64(bits_host(h.indexed(bf16_dev(x), i32_dev(ids), f32_dev(tw))))
     torch.cuda.synchronize()
+    del h
     assert np.all(np.isfinite(out))
-    sample = np.array([0, wl.T // 2, wl.T - 1])
-    ref = O.moe_indexed(x, ids, tw, _provider(w), E=wl.E, tokens=sample)
-    check_tol(out[sample], ref, f"{wl.name} tokens {sample.tolist()}")
+    tok = cover_tokens(ids, first=[0, wl.T - 1])
+    req = RowRequests()
+    place = indexed_request(req, x, ids, tok)
+    req.run(w, "TP8 shard, 384 experts, I=256")
+    ref = indexed_reference(req, place, tw, tok, wl.H)
+    check_tol(out[tok], ref, f"{wl.name}: {len(tok)} tokens covering every expert")
 
 
 def test_full_tiny_config_every_token():
