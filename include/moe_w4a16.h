@@ -316,6 +316,28 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* h, const uint16_t* a, int
                                   void* ws, size_t ws_bytes, const moe_tuning_t* ovr,
                                   moe_stream_t stream);
 
+/* Indexed layout without allocation, for callers that cannot allocate
+ * device memory: code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same layer, kernels and results as
+ * moe_w4a16_indexed with routing = NULL (aligned internally), but the
+ * workspace is a fixed device array inside the library,
+ * MOE_NOALLOC_SCRATCH_BYTES bytes on each GPU the library runs on, held until
+ * the process ends; the caller passes only inputs and outputs.
+ *   x, topk_ids, topk_w, out, ovr: as for moe_w4a16_indexed
+ * The call allocates nothing (no hipMalloc / hipFree, no library routine that
+ * allocates). Every call on one GPU shares that GPU's array and leaves the
+ * last call's contents in it: calls that overlap on one GPU (two streams, two
+ * threads) race and must be serialised by the caller.
+ * Errors: as moe_w4a16_indexed, and WORKSPACE_TOO_SMALL (before anything is
+ * enqueued) when the call's workspace (moe_workspace_bytes(h,
+ * MOE_MODE_INDEXED, T, topk, T, ovr)) exceeds the array: 128 MiB holds the
+ * Kimi decode shape (448 tokens, top-8, 384 experts, hidden 7168,
+ * intermediate 2048) and smaller ones. */
+#define MOE_NOALLOC_SCRATCH_BYTES (128u << 20)
+moe_status_t moe_w4a16_indexed_noalloc(const moe_weights_t* h, const uint16_t* x, int32_t T,
+                                       int32_t topk, const int32_t* topk_ids, const float* topk_w,
+                                       uint16_t* out, const moe_tuning_t* ovr, moe_stream_t stream);
+
 /* Masked layout (Chord page, "Grouped SM90 kernels": expected_m is a
  * positive integer that picks the launch, masked_m holds the valid count
  * per expert, the output is flat even for a 3-D a3, rows past the valid

@@ -245,3 +245,29 @@ def test_schedule_choice_by_rows_per_expert(L):
     st = L.moe_w4a16_indexed(tail.h, fake, 320, 4, fake, fake, None, fake, fake, 1 << 40,
                              ctypes.byref(large), None)
     assert st == M.MOE_ERR_OVERRIDE_REJECTED
+
+
+def test_noalloc_scratch_size_and_host_checks(L):
+    """The fixed scratch array behind moe_w4a16_indexed_noalloc holds the
+    Kimi decode shape's workspace; a call that needs more fails with
+    WORKSPACE_TOO_SMALL on the host, before anything is enqueued."""
+    text = open(HEADER).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == M.NOALLOC_SCRATCH_BYTES
+    d = desc(E=384, H=7168, I=2048)
+    h = L.moe_plan_create(ctypes.byref(d))
+    assert h
+    try:
+        need = L.moe_workspace_bytes(h, M.MOE_MODE_INDEXED, 448, 8, 448, None)
+        assert 0 < need <= M.NOALLOC_SCRATCH_BYTES, need
+        big = L.moe_workspace_bytes(h, M.MOE_MODE_INDEXED, 4096, 8, 4096, None)
+        assert big > M.NOALLOC_SCRATCH_BYTES
+        st = L.moe_w4a16_indexed_noalloc(h, 16, 4096, 8, 16, 16, 16, None, None)
+        assert st == 5 and b"scratch" in L.moe_last_error()          # WORKSPACE_TOO_SMALL
+        # fits: stops at the plan's missing weights, before any HIP call
+        st = L.moe_w4a16_indexed_noalloc(h, 16, 448, 8, 16, 16, 16, None, None)
+        assert st == 1 and b"no prepared weights" in L.moe_last_error()
+        assert L.moe_w4a16_indexed_noalloc(h, 16, 448, 8, None, 16, 16, None, None) == 1   # NULL ids
+        assert L.moe_w4a16_indexed_noalloc(h, 16, 0, 8, 16, 16, 16, None, None) == 0       # nothing to do
+    finally:
+        L.moe_release_weights(h)

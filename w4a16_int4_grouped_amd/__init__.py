@@ -32,6 +32,9 @@ MOE_MODE_CONTIGUOUS = 1
 MOE_MODE_MASKED = 2
 MODES = {"indexed": MOE_MODE_INDEXED, "contiguous": MOE_MODE_CONTIGUOUS, "masked": MOE_MODE_MASKED}
 
+# bytes of the fixed device scratch array behind moe_w4a16_indexed_noalloc
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
 MOE_SCALE_BF16 = 1
 MOE_PACK_INT32_LOW_NIBBLE_FIRST_K = 1
 
@@ -39,7 +42,7 @@ EXPORTS = [
     "moe_abi_version", "moe_last_error", "moe_status_string", "moe_prepared_bytes",
     "moe_prepare_weights", "moe_release_weights", "moe_plan_create", "moe_routing_block", "moe_routing_bytes",
     "moe_routing_layout", "moe_align", "moe_align_ep", "moe_permute", "moe_workspace_bytes", "moe_w4a16_indexed",
-    "moe_w4a16_contiguous", "moe_w4a16_masked", "moe_w4a16_gate_up", "moe_w4a16_down", "moe_swiglu",
+    "moe_w4a16_indexed_noalloc", "moe_w4a16_contiguous", "moe_w4a16_masked", "moe_w4a16_gate_up", "moe_w4a16_down", "moe_swiglu",
     "moe_dequant_weights", "moe_describe",
     "moe_profile_enable", "moe_profile_reset", "moe_profile_read",
 ]
@@ -109,6 +112,7 @@ def lib() -> ctypes.CDLL:
         "moe_permute": (S, [P, P, I32, I32, ctypes.POINTER(Tuning), P, P, P, P, P]),
         "moe_workspace_bytes": (SZ, [P, I32, I32, I32, I32, ctypes.POINTER(Tuning)]),
         "moe_w4a16_indexed": (S, [P, P, I32, I32, P, P, P, P, P, SZ, ctypes.POINTER(Tuning), P]),
+        "moe_w4a16_indexed_noalloc": (S, [P, P, I32, I32, P, P, P, ctypes.POINTER(Tuning), P]),
         "moe_w4a16_contiguous": (S, [P, P, I32, P, P, P, I32, I32, P, P, SZ, ctypes.POINTER(Tuning), P]),
         "moe_w4a16_masked": (S, [P, P, I32, P, I32, P, P, SZ, ctypes.POINTER(Tuning), P]),
         "moe_w4a16_gate_up": (S, [P, P, I32, I32, P, P, ctypes.POINTER(Tuning), P]),
@@ -256,6 +260,14 @@ class PreparedWeights:
         check(lib().moe_w4a16_indexed(self.handle, _ptr(x), T, topk, _ptr(topk_ids), _ptr(topk_w),
                                       _ptr(routing), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                       _tuning(ovr), _stream(stream)))
+        return out
+
+    def indexed_noalloc(self, x, topk_ids, topk_w, out, ovr=None, stream=None):
+        """The indexed layer on the library's fixed scratch array: allocates
+        nothing, so `out` must be given."""
+        T, topk = topk_ids.shape
+        check(lib().moe_w4a16_indexed_noalloc(self.handle, _ptr(x), T, topk, _ptr(topk_ids), _ptr(topk_w),
+                                              _ptr(out), _tuning(ovr), _stream(stream)))
         return out
 
     def contiguous(self, a, m_indices, row_src=None, topk_w=None, T=0, topk=0, out=None, ws=None,

@@ -916,6 +916,71 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   return ok();
 }
 
+}  // extern "C"
+
+// --------------------------------------------------------------------------
+// The indexed layer without allocation: its workspace (the routing made by
+// the internal alignment, the BF16 intermediate and the weighted rows) lives
+// in a fixed device array of this library, so a caller that cannot allocate
+// device memory (graph capture, a tight serving loop) passes only inputs and
+// outputs. Each GPU holds its own copy of the array at its own address; the
+// host-side name `scratch` is not that address, so the address is taken once
+// per device with hipGetSymbolAddress and only that pointer reaches kernels.
+// --------------------------------------------------------------------------
+
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (h->device, made
+// current by set_device), taken on first use.
+moe_status_t scratch_ptr(int device, void** out) {
+  if (device < 0 || device >= kMaxDevices)
+    return fail(MOE_ERR_INVALID_ARG, "device %d outside 0..%d", device, kMaxDevices - 1);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned(ptr, kAlign))
+      return fail(MOE_ERR_HIP, "scratch array at %p: not 256-byte aligned", ptr);
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_w4a16_indexed_noalloc(const moe_weights_t* hc, const uint16_t* x, int32_t T,
+                                       int32_t topk, const int32_t* topk_ids, const float* topk_w,
+                                       uint16_t* out, const moe_tuning_t* ovr, moe_stream_t stream) {
+  moe_weights_t* h = const_cast<moe_weights_t*>(hc);
+  moe_status_t st = check_handle(h, MOE_MODE_INDEXED);
+  if (st != MOE_OK) return st;
+  if ((st = check_topk(h, T, topk)) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if (!topk_ids) return fail(MOE_ERR_INVALID_ARG, "NULL topk_ids (this entry point aligns internally)");
+  const size_t need = moe_workspace_bytes(h, MOE_MODE_INDEXED, T, topk, T, ovr);
+  if (!need) return ovr && large_m_rejected(h, ovr) ? MOE_ERR_OVERRIDE_REJECTED : MOE_ERR_INVALID_ARG;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
+                "this call needs %zu bytes of workspace; the fixed scratch array holds %zu "
+                "(use moe_w4a16_indexed with a workspace of its own)",
+                need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  if ((st = set_device(h)) != MOE_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_ptr(h->device, &ws)) != MOE_OK) return st;
+  return moe_w4a16_indexed(h, x, T, topk, topk_ids, topk_w, nullptr, out, ws,
+                           (size_t)MOE_NOALLOC_SCRATCH_BYTES, ovr, stream);
+}
+
 // One grouped GEMM of the indexed layout with a BF16 output at routing-slot
 // rows (the unfused step sequence): mat 13 (x gathered through the routing,
 // output gate | up) or 2 (a rows at their slots).
