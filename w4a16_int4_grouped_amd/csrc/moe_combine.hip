@@ -2,8 +2,8 @@
 // layer's combine: the routing weight applies after the second GEMM).
 //
 // The second GEMM stores each routed row already weighted, w * y, at its flat
-// index f = t*topk + j, as 24-bit floats (store_y24: FP32 rounded to 16
-// significant bits). This kernel adds a token's top-k rows in FP32 in
+// index f = t*topk + j, as 16-bit integers with a power-of-two scale per 8
+// positions (store_y16). This kernel adds a token's top-k rows in FP32 in
 // ascending j and rounds once to BF16. No atomics: the accumulator of an
 // atomic scatter-add is shared by workgroups on all XCDs, so every add would
 // be performed past the per-XCD L2 at a fraction of the streaming rate.
@@ -26,20 +26,21 @@ __device__ __forceinline__ f32x4_t keep_if(f32x4_t y, bool v) {
   return r;
 }
 
-// One thread per (token, 8 adjacent positions of a row: two groups of 4 in
-// the W2 epilogue's lane-contiguous order, store_y24), read with one 16-byte
-// and one 8-byte load per row. A row f is summed when valid[f] >= 0 (the slot
-// of f in the indexed layout's routing; 0 for the contiguous layout's rows).
-// With a routing header that does not describe (E, block, T*topk) nothing was
-// computed and the result is zero, as for the GEMMs. A token's rows are loaded
-// kRowBatch at a time before any is added, so a thread keeps up to 8 rows'
-// loads in flight instead of one. Rows still add in ascending j; a skipped row
-// (another GPU's expert) costs no read and adds nothing (the sum starts at +0
-// and never becomes -0, so adding +0 is exact).
+// One thread per (token, 8 adjacent positions of a row: one scale group, two
+// groups of 4 features in the W2 epilogue's lane-contiguous order, store_y16),
+// read with one 16-byte load and one byte per row. A row f is summed when
+// valid[f] >= 0 (the slot of f in the indexed layout's routing; 0 for the
+// contiguous layout's rows). With a routing header that does not describe
+// (E, block, T*topk) nothing was computed and the result is zero, as for the
+// GEMMs. A token's rows are loaded kRowBatch at a time before any is added, so
+// a thread keeps up to 8 rows' loads in flight instead of one. Rows still add
+// in ascending j; a skipped row (another GPU's expert) costs no read and adds
+// nothing (its integers are 0, and adding 0 * scale = +0 to a sum that starts
+// at +0 and never becomes -0 is exact).
 constexpr int kRowBatch = 8;
 
-__global__ __launch_bounds__(256) void combine_rows(const uint16_t* __restrict__ yhi,
-                                                    const uint8_t* __restrict__ ylo,
+__global__ __launch_bounds__(256) void combine_rows(const uint16_t* __restrict__ yq,
+                                                    const uint8_t* __restrict__ ye,
                                                     const int32_t* __restrict__ valid,
                                                     const int32_t* __restrict__ hdr, int E, int block,
                                                     int T, int topk, int H, int ld,
@@ -59,23 +60,20 @@ __global__ __launch_bounds__(256) void combine_rows(const uint16_t* __restrict__
       bool use[kRowBatch];
 #pragma unroll
       for (int u = 0; u < kRowBatch; ++u) use[u] = j0 + u < topk && valid[f0 + j0 + u] >= 0;
-      u32x4_t h[kRowBatch];
-      u32x2_t l[kRowBatch];
+      u32x4_t d[kRowBatch];
+      uint32_t eb[kRowBatch];
 #pragma unroll
       for (int u = 0; u < kRowBatch; ++u) {
-        h[u] = u32x4_t{0u, 0u, 0u, 0u};   // +0 in every value
-        l[u] = u32x2_t{0u, 0u};
+        d[u] = u32x4_t{0u, 0u, 0u, 0u};   // integers 0: adds +0
+        eb[u] = 128u;
         if (use[u]) {
           const size_t idx = (size_t)(f0 + j0 + u) * ld + p0;
-          h[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(yhi + idx));
-          l[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(ylo + idx));
+          d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(yq + idx));
+          eb[u] = __builtin_nontemporal_load(ye + idx / 8);
         }
       }
 #pragma unroll
-      for (int u = 0; u < kRowBatch; ++u) {
-        acc[0] += unpack_y24(h[u][0], h[u][1], l[u][0]);
-        acc[1] += unpack_y24(h[u][2], h[u][3], l[u][1]);
-      }
+      for (int u = 0; u < kRowBatch; ++u) add_y16(acc, d[u], y16_scale(eb[u]));
     }
   }
 #pragma unroll
@@ -236,13 +234,13 @@ hipError_t launch_splitk_combine(const float* part, int S, const int32_t* slot_o
   return hipGetLastError();
 }
 
-hipError_t launch_combine_rows(const uint16_t* yhi, const uint8_t* ylo, int ld, const int32_t* valid,
+hipError_t launch_combine_rows(const uint16_t* yq, const uint8_t* ye, int ld, const int32_t* valid,
                                const int32_t* hdr, int E, int block, int T, int topk, int H, uint16_t* out,
                                hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (ld % 64 || ld < H || H % 4) return hipErrorInvalidValue;   // rows in 64-feature blocks (store_y24)
+  if (ld % 64 || ld < H || H % 4) return hipErrorInvalidValue;   // rows in 64-feature blocks (store_y16)
   const int pieces = (H + 63) / 64 * 8;   // 8-position pieces of a token's row blocks
-  hipLaunchKernelGGL(combine_rows, dim3((pieces + 255) / 256, T), dim3(256), 0, s, yhi, ylo, valid, hdr, E,
+  hipLaunchKernelGGL(combine_rows, dim3((pieces + 255) / 256, T), dim3(256), 0, s, yq, ye, valid, hdr, E,
                      block, T, topk, H, ld, out);
   return hipGetLastError();
 }

@@ -183,55 +183,79 @@ __device__ __forceinline__ float swiglu(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
-// Weighted rows w*y of the second GEMM, kept for the combine as 24-bit
-// floats: the FP32 value rounded to its upper 24 bits (sign, exponent and
-// 15 stored mantissa bits, to nearest with ties away from zero), split into
-// a 16-bit high plane and an 8-bit low plane of [rows][ld] each. Each value
-// is then within 2^-16 of the FP32 one in relative terms (the layer's BF16
-// output rounds at 2^-9), and a row costs 3 bytes per feature instead of 4
-// in the GEMM's writes and the combine's reads.
+// Weighted rows w*y of the second GEMM, kept for the combine as 16-bit
+// integers with one power-of-two scale per 8 adjacent positions: a group of
+// 8 values v with max|v| < 2^e (e from frexp, clamped to >= -100) stores
+// n = round_to_nearest_even(v * 2^(14 - e)), |n| <= 2^14, in an int16 plane of
+// [rows][ld] and the byte e + 128 in an exponent plane of [rows][ld / 8]; the
+// value read back is n * 2^(e - 14), within 2^-15 * 2^e <= 2^-14 * max|v| of
+// v. The layer's output is a BF16 sum of a token's top-k rows, rounded at
+// 2^-9 of its magnitude, so this error stays four orders of magnitude below
+// the output's own rounding; a row costs 2.125 bytes per feature in the GEMM's
+// writes and the combine's reads.
 //
 // Within each 64-feature block (one row group of 4 MFMA tiles), feature
 // n = 16*mt + 4*q + i sits at position 16*q + 4*mt + i: the 16 values a lane
-// q holds for a token row (4 per tile mt) are adjacent, so a lane writes
-// them with full 16-byte stores and the 4 lanes of a row fill 128 bytes of
-// the high plane (with plain [n] order each lane would write 8- and 4-byte
-// pieces 32 bytes apart, which measured 40 % slower on the TP8 shard's W2).
+// q holds for a token row (4 per tile mt) are adjacent, so a lane writes them
+// with full 16-byte stores and the 4 lanes of a row fill 128 contiguous bytes
+// of the int16 plane (with plain [n] order each lane would write pieces 32
+// bytes apart).
 
-// Stores G groups of 4 values (tiles mt0 .. mt0 + G - 1 of lane q) at row
-// element idx = block + 16*q + 4*mt0 (G = 4: mt0 = 0; G = 2: mt0 even).
+constexpr float kRoundMagic = 12582912.0f;   // 1.5 * 2^23: x + magic has ulp 1
+
+// Stores G groups of 4 values w * v[g] (tiles mt0 .. mt0 + G - 1 of lane q)
+// at row position idx = row * ld + block + 16*q + 4*mt0 (G = 4: mt0 = 0; G = 2:
+// mt0 even), idx a multiple of 8: G / 2 scale groups of 8.
 template <int G>
-__device__ __forceinline__ void store_y24(uint16_t* __restrict__ hi, uint8_t* __restrict__ lo, size_t idx,
-                                          const f32x4_t (&v)[G]) {
+__device__ __forceinline__ void store_y16(uint16_t* __restrict__ yq, uint8_t* __restrict__ ye, size_t idx,
+                                          float w, const f32x4_t (&v)[G]) {
   static_assert(G == 2 || G == 4, "2 or 4 groups");
-  uint32_t h[2 * G], l[G];
+  uint32_t d[2 * G];
+  uint32_t eb[G / 2];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    uint32_t b[4];
+  for (int k = 0; k < G / 2; ++k) {
+    float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = __float_as_uint(v[g][i]) + 0x80u;
-    h[2 * g] = (b[0] >> 16) | (b[1] & 0xFFFF0000u);
-    h[2 * g + 1] = (b[2] >> 16) | (b[3] & 0xFFFF0000u);
-    l[g] = ((b[0] >> 8) & 0xFFu) | (b[1] & 0xFF00u) | ((b[2] & 0xFF00u) << 8) | ((b[3] & 0xFF00u) << 16);
+    for (int g = 2 * k; g < 2 * k + 2; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(v[g][i]));
+    // fl(amax * |w|) < 2^e implies |v * w| < 2^e for every value of the group
+    const int e = max(__builtin_amdgcn_frexp_expf(amax * fabsf(w)), -100);
+    const float sc = __builtin_amdgcn_ldexpf(w, 14 - e);   // exact: a power-of-two multiple of w
+    eb[k] = (uint32_t)(e + 128);
+#pragma unroll
+    for (int g = 2 * k; g < 2 * k + 2; ++g) {
+      uint32_t x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = __float_as_uint(__builtin_fmaf(v[g][i], sc, kRoundMagic));
+      // low halves: the rounded integers, two's complement
+      d[2 * g] = __builtin_amdgcn_perm(x[1], x[0], 0x05040100u);
+      d[2 * g + 1] = __builtin_amdgcn_perm(x[3], x[2], 0x05040100u);
+    }
   }
 #pragma unroll
   for (int k = 0; k < G / 2; ++k)
-    *reinterpret_cast<u32x4_t*>(hi + idx + 8 * k) = u32x4_t{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
+    *reinterpret_cast<u32x4_t*>(yq + idx + 8 * k) = u32x4_t{d[4 * k], d[4 * k + 1], d[4 * k + 2], d[4 * k + 3]};
   if constexpr (G == 4)
-    *reinterpret_cast<u32x4_t*>(lo + idx) = u32x4_t{l[0], l[1], l[2], l[3]};
+    *reinterpret_cast<uint16_t*>(ye + idx / 8) = (uint16_t)(eb[0] | (eb[1] << 8));
   else
-    *reinterpret_cast<u32x2_t*>(lo + idx) = u32x2_t{l[0], l[1]};
+    ye[idx / 8] = (uint8_t)eb[0];
 }
 
-// One group of 4 values stored by store_y24 (high-plane dwords ha, hb and
-// low-plane dword l), as FP32.
-__device__ __forceinline__ f32x4_t unpack_y24(uint32_t ha, uint32_t hb, uint32_t l) {
-  f32x4_t v;
-  v[0] = __uint_as_float((ha << 16) | ((l & 0xFFu) << 8));
-  v[1] = __uint_as_float((ha & 0xFFFF0000u) | (l & 0xFF00u));
-  v[2] = __uint_as_float((hb << 16) | ((l >> 8) & 0xFF00u));
-  v[3] = __uint_as_float((hb & 0xFFFF0000u) | ((l >> 16) & 0xFF00u));
-  return v;
+// The scale 2^(e - 14) of a group from its stored exponent byte.
+__device__ __forceinline__ float y16_scale(uint32_t eb) {
+  return __uint_as_float((eb - 128u + 127u - 14u) << 23);
+}
+
+// acc += the 8 values of a group (int16 pairs d[0..3], scale sc).
+__device__ __forceinline__ void add_y16(f32x4_t (&acc)[2], const u32x4_t& d, float sc) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float lo = (float)(int32_t)(int16_t)(d[m] & 0xFFFFu);
+    const float hi = (float)((int32_t)d[m] >> 16);
+    acc[m >> 1][2 * (m & 1)] = __builtin_fmaf(lo, sc, acc[m >> 1][2 * (m & 1)]);
+    acc[m >> 1][2 * (m & 1) + 1] = __builtin_fmaf(hi, sc, acc[m >> 1][2 * (m & 1) + 1]);
+  }
 }
 
 }  // namespace moe

@@ -212,11 +212,11 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c, 
       }
       if (f < 0 || f >= p.sentinel) continue;
       const float w = p.topk_w[f];
-      if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (store_y24)
+      if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (store_y16)
         f32x4_t v[kMT];
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) v[mt] = w * acc[mt][nt];
-        store_y24<kMT>(p.yhi, p.ylo, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, v);
+        for (int mt = 0; mt < kMT; ++mt) v[mt] = acc[mt][nt];
+        store_y16<kMT>(p.yq, p.ye, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, w, v);
       }
     } else {
       if constexpr (SET == SET_ROUTED) {
@@ -287,11 +287,11 @@ __device__ __forceinline__ void epilogue_meta(const GemmParams& p, const TileCtx
       }
     } else if constexpr (EPI == EPI_COMBINE) {
       const float w = m.w[r];
-      if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (store_y24)
+      if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (store_y16)
         f32x4_t v[kMT];
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) v[mt] = w * acc[mt][nt];
-        store_y24<kMT>(p.yhi, p.ylo, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, v);
+        for (int mt = 0; mt < kMT; ++mt) v[mt] = acc[mt][nt];
+        store_y16<kMT>(p.yq, p.ye, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, w, v);
       }
     } else {
       uint16_t* dst = p.out + (size_t)slot * p.out_ld;

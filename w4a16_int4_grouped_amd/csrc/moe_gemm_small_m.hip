@@ -338,11 +338,11 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
         }
         if (f < 0 || f >= p.sentinel) continue;
         const float w = p.topk_w[f];
-        if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (store_y24)
+        if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (store_y16)
           f32x4_t v[kMT];
 #pragma unroll
-          for (int mt = 0; mt < kMT; ++mt) v[mt] = w * acc[mt][nt];
-          store_y24<kMT>(p.yhi, p.ylo, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, v);
+          for (int mt = 0; mt < kMT; ++mt) v[mt] = acc[mt][nt];
+          store_y16<kMT>(p.yq, p.ye, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, w, v);
         }
       } else if constexpr (EPI == EPI_PARTIAL) {
         const int f = p.sorted_ids[slot];
@@ -539,11 +539,11 @@ __device__ __forceinline__ void job_epilogue(const GemmParams& p, const f32x4_t 
       }
     } else if constexpr (EPI == EPI_COMBINE) {
       const float w = p.topk_w[f];
-      if (b.rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (store_y24)
+      if (b.rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (store_y16)
         f32x4_t v[kMT];
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) v[mt] = w * acc[mt][nt];
-        store_y24<kMT>(p.yhi, p.ylo, (size_t)f * p.yrows_ld + b.rg * kRowsRG + (lane >> 4) * 16, v);
+        for (int mt = 0; mt < kMT; ++mt) v[mt] = acc[mt][nt];
+        store_y16<kMT>(p.yq, p.ye, (size_t)f * p.yrows_ld + b.rg * kRowsRG + (lane >> 4) * 16, w, v);
       }
     } else {
       uint16_t* dst = p.out + (size_t)slot * p.out_ld;

@@ -157,10 +157,10 @@ __device__ __forceinline__ void wide_epilogue(const GemmParams& p, const WideCtx
       v[1] = pack_bf16x2(swiglu(g[2], u[2]), swiglu(g[3], u[3]));
       *reinterpret_cast<u32x2_t*>(dst) = v;
     } else if constexpr (EPI == EPI_COMBINE) {
-      if (c.rg * kRowsRG < p.N) {   // tiles mt0, mt0 + 1 of the row group, lane-contiguous (store_y24)
-        const f32x4_t v[2] = {wv[nt] * acc[0][nt], wv[nt] * acc[1][nt]};
+      if (c.rg * kRowsRG < p.N) {   // tiles mt0, mt0 + 1 of the row group, lane-contiguous (store_y16)
+        const f32x4_t v[2] = {acc[0][nt], acc[1][nt]};
         const size_t idx = (size_t)fv[nt] * p.yrows_ld + c.rg * kRowsRG + (lane >> 4) * 16 + c.mt0 * 4;
-        store_y24<2>(p.yhi, p.ylo, idx, v);
+        store_y16<2>(p.yq, p.ye, idx, wv[nt], v);
       }
     } else {
       uint16_t* dst = p.out + (size_t)slot * p.out_ld;
