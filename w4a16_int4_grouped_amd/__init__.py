@@ -15,8 +15,8 @@ import ctypes
 import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-# MOE_W4A16_LIBRARY: load another build of the same ABI (e.g. for A/B timing)
-LIB_PATH = os.environ.get("MOE_W4A16_LIBRARY") or os.path.join(PKG_DIR, "libmoe_w4a16.so")
+# the in-tree build of csrc/ (w4a16_int4_grouped_amd/build.py); no other library stands in for it
+LIB_PATH = os.path.join(PKG_DIR, "libmoe_w4a16.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = 1
