@@ -430,7 +430,7 @@ moe_status_t check_topk(const moe_weights_t* h, int T, int topk) {
 size_t yrow_ld(const moe_weights_t* h) { return ((size_t)h->desc.hidden + 63) / 64 * 64; }
 
 struct WsLayout {
-  size_t off_a = 0, off_y = 0, off_ye = 0, off_part = 0, off_queue = 0, off_check = 0, off_valid = 0,
+  size_t off_a = 0, off_y = 0, off_part = 0, off_queue = 0, off_check = 0, off_valid = 0,
          off_routing = 0, total = 0;
 };
 
@@ -441,10 +441,8 @@ WsLayout ws_indexed(const moe_weights_t* h, int T, int topk, int block, const Sc
   size_t o = 0;
   w.off_a = o;
   o = round_up(o + (size_t)R.cap * h->desc.inter * 2, kAlign);
-  w.off_y = o;   // weighted rows: int16 plane (2 bytes per feature), then exponent plane (1 byte per 8)
+  w.off_y = o;   // weighted rows: 16-bit integers with their group scales (2 bytes per feature)
   o = round_up(o + (size_t)T * topk * yrow_ld(h) * 2, kAlign);
-  w.off_ye = o;
-  o = round_up(o + (size_t)T * topk * yrow_ld(h) / 8, kAlign);
   // split-K partials: [ksplit][T*topk][N] FP32 per GEMM (one at a time)
   w.off_part = o;
   const size_t p13 = sc.ksplit13 > 1 ? (size_t)sc.ksplit13 * 2 * h->desc.inter : 0;
@@ -466,10 +464,8 @@ WsLayout ws_rows(const moe_weights_t* h, int64_t rows, int64_t flat_rows) {
   size_t o = 0;
   w.off_a = o;
   o = round_up(o + (size_t)rows * h->desc.inter * 2, kAlign);
-  w.off_y = o;   // weighted rows: int16 plane (2 bytes per feature), then exponent plane (1 byte per 8)
+  w.off_y = o;   // weighted rows: 16-bit integers with their group scales (2 bytes per feature)
   o = round_up(o + (size_t)flat_rows * yrow_ld(h) * 2, kAlign);
-  w.off_ye = o;
-  o = round_up(o + (size_t)flat_rows * yrow_ld(h) / 8, kAlign);
   w.off_valid = w.off_routing = o;
   o = round_up(o + (size_t)flat_rows * 4, kAlign);
   w.off_check = o;   // counters of the validation mode
@@ -837,7 +833,6 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   const int H = h->desc.hidden, I = h->desc.inter, E = h->desc.num_experts;
   uint16_t* a_ws = (uint16_t*)(wsb + W.off_a);
   uint16_t* yq = (uint16_t*)(wsb + W.off_y);
-  uint8_t* ye = (uint8_t*)(wsb + W.off_ye);
   GemmParams p{};
   p.counts = rt + R.off_counts;
   p.offsets = rt + R.off_offsets;
@@ -894,7 +889,6 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
   p2.src = a_ws;
   p2.src_ld = I;
   p2.yq = yq;
-  p2.ye = ye;
   p2.topk_w = topk_w;
   p2.yrows_ld = (int64_t)yrow_ld(h);
   if (split2) {   // reduced by the combine
@@ -909,7 +903,7 @@ moe_status_t moe_w4a16_indexed(const moe_weights_t* hc, const uint16_t* x, int32
     e = run("combine_topk", s, [&] {
       return split2 ? launch_splitk_combine(part, sc.ksplit2, rt + R.off_slot_of, rt, E, B, topk_w, T, topk,
                                             H, out, s)
-                    : launch_combine_rows(yq, ye, (int)yrow_ld(h), rt + R.off_slot_of, rt, E, B, T, topk, H,
+                    : launch_combine_rows(yq, (int)yrow_ld(h), rt + R.off_slot_of, rt, E, B, T, topk, H,
                                           out, s);
     });
   if (e != hipSuccess) return hip_fail(e, "indexed launch");
@@ -1091,7 +1085,6 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
   const int H = h->desc.hidden, I = h->desc.inter;
   uint16_t* a_ws = (uint16_t*)(wsb + W.off_a);
   uint16_t* yq = (uint16_t*)(wsb + W.off_y);
-  uint8_t* ye = (uint8_t*)(wsb + W.off_ye);
   int32_t* valid = (int32_t*)(wsb + W.off_valid);
   hipError_t e = hipSuccess;
   if (h->env.validate) {   // the row-validity map serves as the row_src scratch
@@ -1133,7 +1126,6 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
   p2.src_ld = I;
   if (row_src) {
     p2.yq = yq;
-  p2.ye = ye;
     p2.topk_w = topk_w;
     p2.yrows_ld = (int64_t)yrow_ld(h);
     if (e == hipSuccess && T > 0)
@@ -1144,7 +1136,7 @@ moe_status_t moe_w4a16_contiguous(const moe_weights_t* hc, const uint16_t* a, in
       e = run_gemm(2, sc, p2, SET_BLOCKS, EPI_COMBINE, s, h->env);
     if (e == hipSuccess && T > 0)
       e = run("combine_topk", s, [&] {
-        return launch_combine_rows(yq, ye, (int)yrow_ld(h), valid, nullptr, h->desc.num_experts, 0, T, topk,
+        return launch_combine_rows(yq, (int)yrow_ld(h), valid, nullptr, h->desc.num_experts, 0, T, topk,
                                    H, out, s);
       });
   } else {

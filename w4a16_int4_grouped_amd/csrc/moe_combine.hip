@@ -28,7 +28,7 @@ __device__ __forceinline__ f32x4_t keep_if(f32x4_t y, bool v) {
 
 // One thread per (token, 8 adjacent positions of a row: one scale group, two
 // groups of 4 features in the W2 epilogue's lane-contiguous order, store_y16),
-// read with one 16-byte load and one byte per row. A row f is summed when
+// read with one 16-byte load per row. A row f is summed when
 // valid[f] >= 0 (the slot of f in the indexed layout's routing; 0 for the
 // contiguous layout's rows). With a routing header that does not describe
 // (E, block, T*topk) nothing was computed and the result is zero, as for the
@@ -40,7 +40,6 @@ __device__ __forceinline__ f32x4_t keep_if(f32x4_t y, bool v) {
 constexpr int kRowBatch = 8;
 
 __global__ __launch_bounds__(256) void combine_rows(const uint16_t* __restrict__ yq,
-                                                    const uint8_t* __restrict__ ye,
                                                     const int32_t* __restrict__ valid,
                                                     const int32_t* __restrict__ hdr, int E, int block,
                                                     int T, int topk, int H, int ld,
@@ -61,19 +60,16 @@ __global__ __launch_bounds__(256) void combine_rows(const uint16_t* __restrict__
 #pragma unroll
       for (int u = 0; u < kRowBatch; ++u) use[u] = j0 + u < topk && valid[f0 + j0 + u] >= 0;
       u32x4_t d[kRowBatch];
-      uint32_t eb[kRowBatch];
 #pragma unroll
       for (int u = 0; u < kRowBatch; ++u) {
-        d[u] = u32x4_t{0u, 0u, 0u, 0u};   // integers 0: adds +0
-        eb[u] = 128u;
+        d[u] = kY16Zero;   // integers 0: adds +0
         if (use[u]) {
           const size_t idx = (size_t)(f0 + j0 + u) * ld + p0;
           d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(yq + idx));
-          eb[u] = __builtin_nontemporal_load(ye + idx / 8);
         }
       }
 #pragma unroll
-      for (int u = 0; u < kRowBatch; ++u) add_y16(acc, d[u], y16_scale(eb[u]));
+      for (int u = 0; u < kRowBatch; ++u) add_y16(acc, d[u]);
     }
   }
 #pragma unroll
@@ -234,13 +230,13 @@ hipError_t launch_splitk_combine(const float* part, int S, const int32_t* slot_o
   return hipGetLastError();
 }
 
-hipError_t launch_combine_rows(const uint16_t* yq, const uint8_t* ye, int ld, const int32_t* valid,
+hipError_t launch_combine_rows(const uint16_t* yq, int ld, const int32_t* valid,
                                const int32_t* hdr, int E, int block, int T, int topk, int H, uint16_t* out,
                                hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (ld % 64 || ld < H || H % 4) return hipErrorInvalidValue;   // rows in 64-feature blocks (store_y16)
   const int pieces = (H + 63) / 64 * 8;   // 8-position pieces of a token's row blocks
-  hipLaunchKernelGGL(combine_rows, dim3((pieces + 255) / 256, T), dim3(256), 0, s, yq, ye, valid, hdr, E,
+  hipLaunchKernelGGL(combine_rows, dim3((pieces + 255) / 256, T), dim3(256), 0, s, yq, valid, hdr, E,
                      block, T, topk, H, ld, out);
   return hipGetLastError();
 }

@@ -184,34 +184,37 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 }
 
 // Weighted rows w*y of the second GEMM, kept for the combine as 16-bit
-// integers with one power-of-two scale per 8 adjacent positions: a group of
-// 8 values v with max|v| < 2^e (e from frexp, clamped to >= -100) stores
-// n = round_to_nearest_even(v * 2^(14 - e)), |n| <= 2^14, in an int16 plane of
-// [rows][ld] and the byte e + 128 in an exponent plane of [rows][ld / 8]; the
-// value read back is n * 2^(e - 14), within 2^-15 * 2^e <= 2^-14 * max|v| of
-// v. The layer's output is a BF16 sum of a token's top-k rows, rounded at
-// 2^-9 of its magnitude, so this error stays four orders of magnitude below
-// the output's own rounding; a row costs 2.125 bytes per feature in the GEMM's
-// writes and the combine's reads.
+// integers with one power-of-two scale per 8 adjacent positions, the scale's
+// exponent carried in the values' lowest bits. For a group of 8 values v
+// with max|v| * (1 + 2^-13) < 2^e (e from frexp, clamped to >= -100), value
+// i is n_i = round_to_nearest_even(v_i * 2^(14 - e)), |n_i| < 16383, stored as
+// 2 n_i + b_i, where b_0 .. b_7 are the bits of the byte e + 128 (dword j of
+// the group holds values 2j and 2j + 1 and exponent bits j and j + 4). Read
+// back, n_i * 2^(e - 14) is within 2^-15 * 2^e <= 2^-14 * max|v| of v_i. The
+// layer's output is a BF16 sum of a token's top-k rows, rounded at 2^-9 of
+// its magnitude, so the error stays four orders of magnitude below the
+// output's own rounding. A row costs 2 bytes a feature, written in whole
+// 128-byte lines: a separate exponent plane, written in 8-byte pieces from
+// different workgroups, measured 40 us of partial-line writes on the TP8
+// shard's down projection.
 //
 // Within each 64-feature block (one row group of 4 MFMA tiles), feature
 // n = 16*mt + 4*q + i sits at position 16*q + 4*mt + i: the 16 values a lane
 // q holds for a token row (4 per tile mt) are adjacent, so a lane writes them
 // with full 16-byte stores and the 4 lanes of a row fill 128 contiguous bytes
-// of the int16 plane (with plain [n] order each lane would write pieces 32
-// bytes apart).
+// (with plain [n] order each lane would write pieces 32 bytes apart).
 
 constexpr float kRoundMagic = 12582912.0f;   // 1.5 * 2^23: x + magic has ulp 1
+constexpr float kExpGuard = 1.0f + 0x1p-13f;  // keeps |n| below 16383
 
 // Stores G groups of 4 values w * v[g] (tiles mt0 .. mt0 + G - 1 of lane q)
 // at row position idx = row * ld + block + 16*q + 4*mt0 (G = 4: mt0 = 0; G = 2:
 // mt0 even), idx a multiple of 8: G / 2 scale groups of 8.
 template <int G>
-__device__ __forceinline__ void store_y16(uint16_t* __restrict__ yq, uint8_t* __restrict__ ye, size_t idx,
-                                          float w, const f32x4_t (&v)[G]) {
+__device__ __forceinline__ void store_y16(uint16_t* __restrict__ yq, size_t idx, float w,
+                                          const f32x4_t (&v)[G]) {
   static_assert(G == 2 || G == 4, "2 or 4 groups");
   uint32_t d[2 * G];
-  uint32_t eb[G / 2];
 #pragma unroll
   for (int k = 0; k < G / 2; ++k) {
     float amax = 0.f;
@@ -219,40 +222,44 @@ __device__ __forceinline__ void store_y16(uint16_t* __restrict__ yq, uint8_t* __
     for (int g = 2 * k; g < 2 * k + 2; ++g)
 #pragma unroll
       for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(v[g][i]));
-    // fl(amax * |w|) < 2^e implies |v * w| < 2^e for every value of the group
-    const int e = max(__builtin_amdgcn_frexp_expf(amax * fabsf(w)), -100);
+    // fl(fl(amax * |w|) * guard) < 2^e implies |v * w| * 2^(14 - e) < 16383
+    const int e = max(__builtin_amdgcn_frexp_expf(amax * fabsf(w) * kExpGuard), -100);
     const float sc = __builtin_amdgcn_ldexpf(w, 14 - e);   // exact: a power-of-two multiple of w
-    eb[k] = (uint32_t)(e + 128);
+    const uint32_t eb = (uint32_t)(e + 128);
+    const uint32_t sp = eb | (eb << 12);                    // bit j at 0, bit j + 4 at 16, after >> j
 #pragma unroll
     for (int g = 2 * k; g < 2 * k + 2; ++g) {
       uint32_t x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = __float_as_uint(__builtin_fmaf(v[g][i], sc, kRoundMagic));
-      // low halves: the rounded integers, two's complement
-      d[2 * g] = __builtin_amdgcn_perm(x[1], x[0], 0x05040100u);
-      d[2 * g + 1] = __builtin_amdgcn_perm(x[3], x[2], 0x05040100u);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * (g - 2 * k) + jj;   // dword of the group
+        // low halves of the two values (the rounded integers, two's complement)
+        const uint32_t pair = __builtin_amdgcn_perm(x[2 * jj + 1], x[2 * jj], 0x05040100u);
+        const uint32_t bits = sp >> j;
+        d[2 * g + jj] = (bits & 0x00010001u) | ((pair << 1) & ~0x00010001u);
+      }
     }
   }
 #pragma unroll
   for (int k = 0; k < G / 2; ++k)
     *reinterpret_cast<u32x4_t*>(yq + idx + 8 * k) = u32x4_t{d[4 * k], d[4 * k + 1], d[4 * k + 2], d[4 * k + 3]};
-  if constexpr (G == 4)
-    *reinterpret_cast<uint16_t*>(ye + idx / 8) = (uint16_t)(eb[0] | (eb[1] << 8));
-  else
-    ye[idx / 8] = (uint8_t)eb[0];
 }
 
-// The scale 2^(e - 14) of a group from its stored exponent byte.
-__device__ __forceinline__ float y16_scale(uint32_t eb) {
-  return __uint_as_float((eb - 128u + 127u - 14u) << 23);
-}
+// A group of store_y16 that adds nothing: integers 0 and exponent byte 128.
+constexpr u32x4_t kY16Zero = {0u, 0u, 0u, 0x00010000u};
 
-// acc += the 8 values of a group (int16 pairs d[0..3], scale sc).
-__device__ __forceinline__ void add_y16(f32x4_t (&acc)[2], const u32x4_t& d, float sc) {
+// acc += the 8 values of a group (dwords d[0..3] as stored by store_y16).
+__device__ __forceinline__ void add_y16(f32x4_t (&acc)[2], const u32x4_t& d) {
+  const uint32_t t = (d[0] & 0x10001u) | ((d[1] & 0x10001u) << 1) | ((d[2] & 0x10001u) << 2) |
+                     ((d[3] & 0x10001u) << 3);
+  const uint32_t eb = (t & 0xFu) | ((t >> 12) & 0xF0u);
+  const float sc = __uint_as_float((eb - 128u + 127u - 14u) << 23);   // 2^(e - 14)
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const float lo = (float)(int32_t)(int16_t)(d[m] & 0xFFFFu);
-    const float hi = (float)((int32_t)d[m] >> 16);
+    const float lo = (float)((int32_t)(d[m] << 16) >> 17);
+    const float hi = (float)((int32_t)d[m] >> 17);
     acc[m >> 1][2 * (m & 1)] = __builtin_fmaf(lo, sc, acc[m >> 1][2 * (m & 1)]);
     acc[m >> 1][2 * (m & 1) + 1] = __builtin_fmaf(hi, sc, acc[m >> 1][2 * (m & 1) + 1]);
   }

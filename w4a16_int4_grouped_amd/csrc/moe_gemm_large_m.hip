@@ -216,7 +216,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c, 
         f32x4_t v[kMT];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) v[mt] = acc[mt][nt];
-        store_y16<kMT>(p.yq, p.ye, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, w, v);
+        store_y16<kMT>(p.yq, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, w, v);
       }
     } else {
       if constexpr (SET == SET_ROUTED) {
@@ -291,7 +291,7 @@ __device__ __forceinline__ void epilogue_meta(const GemmParams& p, const TileCtx
         f32x4_t v[kMT];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) v[mt] = acc[mt][nt];
-        store_y16<kMT>(p.yq, p.ye, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, w, v);
+        store_y16<kMT>(p.yq, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, w, v);
       }
     } else {
       uint16_t* dst = p.out + (size_t)slot * p.out_ld;
@@ -358,6 +358,7 @@ __device__ __forceinline__ void run_tile_res(const GemmParams& p, const TileCtx&
   {
     const size_t t0 = wq_of(q0);
     load_a_l(fa, wq0 + t0 * (kMT * 64), ws0 + t0 * 64, lane);
+    if constexpr (KCR == 2) load_a_l(fb, wq0 + (t0 + 1) * (kMT * 64), ws0 + (t0 + 1) * 64, lane);
   }
   build_meta<SET, EPI>(p, c, meta);
   __syncthreads();   // the token tile and the row metadata are in LDS
@@ -366,7 +367,6 @@ __device__ __forceinline__ void run_tile_res(const GemmParams& p, const TileCtx&
     // registers across the whole quad loop
     asm volatile("" ::: "memory");
     const int rg = q * 4 + wave;
-    const size_t t0 = wq_of(q);
     const size_t tn = wq_of(q + 1 < q1 ? q + 1 : q);   // past the last quad: a valid repeat
     f32x4_t acc[kMT][NTE];
 #pragma unroll
@@ -374,10 +374,16 @@ __device__ __forceinline__ void run_tile_res(const GemmParams& p, const TileCtx&
 #pragma unroll
       for (int nt = 0; nt < NTE; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if constexpr (KCR == 2) {
-      load_a_l(fb, wq0 + (t0 + 1) * (kMT * 64), ws0 + (t0 + 1) * 64, lane);
+      // both chunks of the next quad are requested before this quad's
+      // epilogue: vmcnt counts stores and loads in one in-order counter, so
+      // a weight load issued after the epilogue's stores could only be
+      // waited for together with them (measured on the TP8 shard's down
+      // projection: the stores then added to the compute time instead of
+      // draining under the next quad's MFMAs)
       mma_chunk_l<NTE, false>(fa, lds[0], c.rd0, acc, mlo, mhi);
       load_a_l(fa, wq0 + tn * (kMT * 64), ws0 + tn * 64, lane);
       mma_chunk_l<NTE, false>(fb, lds[1], c.rd0, acc, mlo, mhi);
+      load_a_l(fb, wq0 + (tn + 1) * (kMT * 64), ws0 + (tn + 1) * 64, lane);
     } else {
       load_a_l(fb, wq0 + tn * (kMT * 64), ws0 + tn * 64, lane);
       mma_chunk_l<NTE, false>(fa, lds[0], c.rd0, acc, mlo, mhi);

@@ -342,7 +342,7 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
           f32x4_t v[kMT];
 #pragma unroll
           for (int mt = 0; mt < kMT; ++mt) v[mt] = acc[mt][nt];
-          store_y16<kMT>(p.yq, p.ye, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, w, v);
+          store_y16<kMT>(p.yq, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, w, v);
         }
       } else if constexpr (EPI == EPI_PARTIAL) {
         const int f = p.sorted_ids[slot];
@@ -543,7 +543,7 @@ __device__ __forceinline__ void job_epilogue(const GemmParams& p, const f32x4_t 
         f32x4_t v[kMT];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) v[mt] = acc[mt][nt];
-        store_y16<kMT>(p.yq, p.ye, (size_t)f * p.yrows_ld + b.rg * kRowsRG + (lane >> 4) * 16, w, v);
+        store_y16<kMT>(p.yq, (size_t)f * p.yrows_ld + b.rg * kRowsRG + (lane >> 4) * 16, w, v);
       }
     } else {
       uint16_t* dst = p.out + (size_t)slot * p.out_ld;

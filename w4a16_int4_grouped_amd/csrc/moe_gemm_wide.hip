@@ -160,7 +160,7 @@ __device__ __forceinline__ void wide_epilogue(const GemmParams& p, const WideCtx
       if (c.rg * kRowsRG < p.N) {   // tiles mt0, mt0 + 1 of the row group, lane-contiguous (store_y16)
         const f32x4_t v[2] = {acc[0][nt], acc[1][nt]};
         const size_t idx = (size_t)fv[nt] * p.yrows_ld + c.rg * kRowsRG + (lane >> 4) * 16 + c.mt0 * 4;
-        store_y16<2>(p.yq, p.ye, idx, wv[nt], v);
+        store_y16<2>(p.yq, idx, wv[nt], v);
       }
     } else {
       uint16_t* dst = p.out + (size_t)slot * p.out_ld;

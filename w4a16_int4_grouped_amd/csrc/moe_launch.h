@@ -57,9 +57,8 @@ struct GemmParams {
   // epilogue targets
   uint16_t* a_out;
   int64_t a_ld;               // SWIGLU
-  uint16_t* yq;               // COMBINE: weighted rows, one per flat index f, as 16-bit
-  uint8_t* ye;                //   integers with a scale per 8 positions (store_y16):
-  const float* topk_w;        //   int16 plane [F][ld] and exponent plane [F][ld / 8]
+  uint16_t* yq;               // COMBINE: weighted rows [F][ld], one per flat index f, as 16-bit
+  const float* topk_w;        //   integers with a scale per 8 positions (store_y16)
   int64_t yrows_ld;           //   ld: features per row (a multiple of 64)
   uint16_t* out;
   int64_t out_ld;             // STORE
@@ -134,9 +133,9 @@ hipError_t launch_count_row_src(const int32_t* m_indices, const int32_t* row_src
 // out[t] = bf16(sum over j ascending of yrows[t*topk + j]) for rows with
 // valid[t*topk + j] >= 0; tokens with no such row get 0. hdr (may be NULL):
 // routing header that must describe (E, block, T*topk), else out = 0.
-// yq/ye: the weighted rows (store_y16), ld features per row (a multiple of
-// 64, >= H).
-hipError_t launch_combine_rows(const uint16_t* yq, const uint8_t* ye, int ld, const int32_t* valid,
+// yq: the weighted rows (store_y16), ld features per row (a multiple of 64,
+// >= H).
+hipError_t launch_combine_rows(const uint16_t* yq, int ld, const int32_t* valid,
                                const int32_t* hdr, int E, int block, int T, int topk, int H, uint16_t* out,
                                hipStream_t s);
 // valid[f] = 0 for every f = row_src[p] of a non-padding contiguous row (the
