@@ -180,20 +180,56 @@ __device__ __forceinline__ void tile_sources(const GemmParams& p, const TileCtx&
 }
 
 // Writes the accumulators of row group rg for token rows tb .. tb + rows.
+// The rows' routing data (slot contents, source row, routing weight) is
+// loaded for all NTE token tiles before any tile is written, so those loads
+// are in flight together: two dependent round trips per tile instead of two
+// per token tile (measured on the prefill down projection: the epilogue took
+// 16 % of the wave time with a round trip per tile).
 template <int SET, int EPI, int NTE>
 __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c, int tb, int rows,
                                          int rg, const f32x4_t (&acc)[kMT][NTE]) {
   const int lane = c.lane;
+  // what each row writes: ROUTED the flat index at its slot; BLOCKS with
+  // COMBINE the flat index its row_src gives; otherwise >= 0. -1: nothing.
+  int fv[NTE];
 #pragma unroll
   for (int nt = 0; nt < NTE; ++nt) {
     const int r = tb + nt * 16 + (lane & 15);
-    if (r >= c.count || r - tb >= rows) continue;
-    const int slot = c.slot0 + r;
+    const bool in = r < c.count && r - tb < rows;
+    const int slot = c.slot0 + (in ? r : tb);   // a row of the tile: always readable
+    if constexpr (SET == SET_ROUTED) {
+      fv[nt] = in ? p.sorted_ids[slot] : -1;
+    } else if constexpr (EPI == EPI_COMBINE) {
+      fv[nt] = in ? p.m_indices[slot] : -1;
+    } else {
+      fv[nt] = in ? 0 : -1;
+    }
+  }
+  if constexpr (SET != SET_ROUTED && EPI == EPI_COMBINE) {
+    int src[NTE];   // loaded for every row (a load under a branch would wait alone)
+#pragma unroll
+    for (int nt = 0; nt < NTE; ++nt) {
+      const int r = min(tb + nt * 16 + (lane & 15), c.count - 1);
+      src[nt] = p.row_src[c.slot0 + r];
+    }
+#pragma unroll
+    for (int nt = 0; nt < NTE; ++nt) fv[nt] = fv[nt] == c.e ? src[nt] : -1;
+  }
+  if constexpr (SET == SET_ROUTED || EPI == EPI_COMBINE) {
+#pragma unroll
+    for (int nt = 0; nt < NTE; ++nt)
+      if (fv[nt] >= p.sentinel) fv[nt] = -1;   // pad slot (ROUTED), out-of-range source (COMBINE)
+  }
+  float wv[NTE];
+  if constexpr (EPI == EPI_COMBINE) {
+#pragma unroll
+    for (int nt = 0; nt < NTE; ++nt) wv[nt] = p.topk_w[fv[nt] >= 0 ? fv[nt] : 0];
+  }
+#pragma unroll
+  for (int nt = 0; nt < NTE; ++nt) {
+    if (fv[nt] < 0) continue;
+    const int slot = c.slot0 + tb + nt * 16 + (lane & 15);
     if constexpr (EPI == EPI_SWIGLU) {
-      if constexpr (SET == SET_ROUTED) {
-        const int f = p.sorted_ids[slot];
-        if (f < 0 || f >= p.sentinel) continue;   // pad slot: never read back
-      }
       uint16_t* dst = p.a_out + (size_t)slot * p.a_ld + rg * 32 + (lane >> 4) * 4;
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
@@ -204,25 +240,13 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const TileCtx& c, 
         *reinterpret_cast<u32x2_t*>(dst + pp * 16) = v;
       }
     } else if constexpr (EPI == EPI_COMBINE) {
-      int f;
-      if constexpr (SET == SET_ROUTED) {
-        f = p.sorted_ids[slot];
-      } else {
-        f = (p.m_indices[slot] == c.e) ? p.row_src[slot] : -1;
-      }
-      if (f < 0 || f >= p.sentinel) continue;
-      const float w = p.topk_w[f];
       if (rg * kRowsRG < p.N) {   // the row group's 64 features, lane-contiguous (store_y16)
         f32x4_t v[kMT];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) v[mt] = acc[mt][nt];
-        store_y16<kMT>(p.yq, (size_t)f * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, w, v);
+        store_y16<kMT>(p.yq, (size_t)fv[nt] * p.yrows_ld + rg * kRowsRG + (lane >> 4) * 16, wv[nt], v);
       }
     } else {
-      if constexpr (SET == SET_ROUTED) {
-        const int f = p.sorted_ids[slot];
-        if (f < 0 || f >= p.sentinel) continue;   // pad slot: output unspecified
-      }
       uint16_t* dst = p.out + (size_t)slot * p.out_ld;
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
