@@ -129,6 +129,30 @@ def test_contiguous_large(E, H, I, T, topk, extra, with_src):
         check_tol(O.bf16_to_f64(bits_host(out))[valid], ref[valid], "contiguous large-M rows")
 
 
+@pytest.mark.parametrize("deal", ["0", "3", "16"])
+def test_xcd_deal_settings(deal, monkeypatch):
+    """The block -> workgroup mapping of the large-M K loop under other unit
+    sizes: 0 (each XCD one contiguous range of blocks), 3 (units that do not
+    divide the block count) and 16 (one unit larger than the routing). Indexed
+    and contiguous, with an expert over several blocks."""
+    require_gpu()
+    monkeypatch.setenv("MOE_W4A16_XCD_DEAL", deal)
+    E, H, I, T, topk = 5, 256, 128, 420, 2
+    log(f"case xcd deal {deal}: E={E} H={H} I={I} T={T} topk={topk}")
+    w = tiny_weights(E, H, I, seed=91)
+    x = synth.activations(92, T, H)
+    ids, tw = synth.zipf_routing(93, T, E, topk)
+    hi = prepare(w, "indexed")
+    assert "schedule=large-M" in hi.describe(T, topk)
+    out = hi.indexed(bf16_dev(x), i32_dev(ids), f32_dev(tw))
+    check_tol(O.bf16_to_f64(bits_host(out)), O.moe_indexed(x, ids, tw, w, E=E), f"indexed deal {deal}")
+    a, m_idx, row_src = O.contiguous_layout(x, ids, E, 128)
+    hc = prepare(w, "contiguous")
+    out = hc.contiguous(bf16_dev(a), i32_dev(m_idx), i32_dev(row_src), f32_dev(tw), T, topk)
+    ref = O.moe_contiguous(a, m_idx, w, row_src=row_src, topk_w=tw, T=T, topk=topk)
+    check_tol(O.bf16_to_f64(bits_host(out)), ref, f"contiguous deal {deal}")
+
+
 def test_masked_large():
     """expected_m >= 80 picks large-M; experts of 0, 1, 129 and 300 valid rows
     (one, two and three tiles); rows past masked_m are NaN."""

@@ -64,10 +64,13 @@ struct EnvOverrides {
   int ksplit = 0;        // MOE_W4A16_KSPLIT: force the small-M split-K factor (tests)
   int validate = 0;      // MOE_W4A16_VALIDATE: synchronous checks of device-side index data
   int wide = 0;          // MOE_W4A16_WIDE: large-M K loop over 256-row tiles (two blocks of an expert)
+  // MOE_W4A16_XCD_DEAL: large-M K loop on blocks, blocks per unit dealt
+  // round-robin to the XCDs (0: each XCD one contiguous range of blocks)
+  int xcd_deal = 2;
   void read() {
-    auto geti = [](const char* k) {
+    auto geti = [](const char* k, int dflt = 0) {
       const char* v = std::getenv(k);
-      return v ? std::atoi(v) : 0;
+      return v ? std::atoi(v) : dflt;
     };
     schedule = geti("MOE_W4A16_SCHEDULE");
     nt = geti("MOE_W4A16_NT");
@@ -77,6 +80,7 @@ struct EnvOverrides {
     ksplit = geti("MOE_W4A16_KSPLIT");
     validate = geti("MOE_W4A16_VALIDATE");
     wide = geti("MOE_W4A16_WIDE");
+    xcd_deal = geti("MOE_W4A16_XCD_DEAL", 2);
   }
 };
 
@@ -214,6 +218,15 @@ hipError_t run_gemm(int mat, const Schedule& sc, const GemmParams& p0, int set, 
       p.total_wg = (p.nsets + 1) / 2 * p.wg_per_set;
       return run(mat == 13 ? "gemm_w13_large_m" : "gemm_w2_large_m", s,
                  [&] { return launch_gemm_wide(p, set, epi, s); });
+    }
+    // K loop on blocks: units of xcd_deal blocks dealt round-robin to the
+    // XCDs, so that runs of equal-cost blocks (one expert's) spread over all
+    // of them (measured on the Zipf prefill: units of 2 blocks -4 % against
+    // contiguous ranges per XCD, 1 or 4 blocks -3 %)
+    if (p.qpw == 0 && set != SET_MASKED && env.xcd_deal > 0) {
+      const int G = env.xcd_deal, units = (p.nsets + G - 1) / G;
+      p.xcd_deal = G;
+      p.total_wg = 8 * ((units + 7) / 8) * G * p.wg_per_set;
     }
     return run(mat == 13 ? "gemm_w13_large_m" : "gemm_w2_large_m", s,
                [&] { return launch_gemm_large_m(p, set, epi, s); });

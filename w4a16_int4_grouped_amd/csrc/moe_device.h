@@ -140,6 +140,22 @@ __device__ __forceinline__ int xcd_remap_active(int b, int active) {
   return base + idx;
 }
 
+// Blocks dealt round-robin to the XCDs in units of G consecutive blocks:
+// unit u (blocks uG .. uG + G - 1) runs on XCD u % 8, an XCD takes its units
+// in order and each block's `wpb` workgroups in a row. Returns the item
+// block * wpb + quad, or -1 past the last of `nblocks`. The grid needs
+// 8 * ceil(ceil(nblocks / G) / 8) * G * wpb workgroups. Runs of blocks of
+// similar cost (one expert's) then spread over all XCDs instead of filling
+// one XCD's range, while a unit's blocks share an XCD.
+__device__ __forceinline__ int xcd_deal_blocks(int b, int nblocks, int wpb, int G) {
+  const int x = b & 7, idx = b >> 3;
+  const int span = G * wpb;
+  const int ul = idx / span, rem = idx - ul * span;
+  const int j = rem / wpb, q = rem - j * wpb;
+  const int blk = (ul * 8 + x) * G + j;
+  return blk < nblocks ? blk * wpb + q : -1;
+}
+
 __device__ __forceinline__ int wave_max(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));

@@ -453,7 +453,14 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m(const GemmParams p) {
         hdr[HDR_T] * hdr[HDR_TOPK] != p.sentinel)
       return;   // routing made for other shapes: compute nothing
     const int nact = min(max(hdr[HDR_TOTAL], 0) / kBM, p.nsets);
-    logical = xcd_remap_active(blockIdx.x, nact * p.wg_per_set);
+    if (KCR == 0 && p.xcd_deal) {
+      logical = xcd_deal_blocks(blockIdx.x, nact, p.wg_per_set, p.xcd_deal);
+    } else {
+      logical = xcd_remap_active(blockIdx.x, nact * p.wg_per_set);
+    }
+    if (logical < 0) return;
+  } else if (KCR == 0 && SET == SET_BLOCKS && p.xcd_deal) {
+    logical = xcd_deal_blocks(blockIdx.x, p.nsets, p.wg_per_set, p.xcd_deal);
     if (logical < 0) return;
   } else {
     logical = xcd_remap(blockIdx.x, p.total_wg);

@@ -38,6 +38,7 @@ struct GemmParams {
   int32_t* queue;        // dispatch 2: job counter, zero at launch
   int nsets;             // row sets (experts or blocks)
   int total_wg;
+  int xcd_deal;          // large-M K loop on blocks: units of xcd_deal blocks dealt round-robin to the XCDs (0: off)
   // row sets
   const int32_t* counts;
   const int32_t* offsets;
