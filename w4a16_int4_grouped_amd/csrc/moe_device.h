@@ -72,11 +72,17 @@ __device__ __forceinline__ u32x4_t dq8(uint32_t w, const GroupScale& g, uint32_t
   const f16x2_t r1 = __builtin_bit_cast(f16x2_t, and_or(w, 0x00F000F0u, magic_hi));    // q1, q5
   const f16x2_t r2 = __builtin_bit_cast(f16x2_t, and_or(w8, 0x000F000Fu, magic_lo));   // q2, q6
   const f16x2_t r3 = __builtin_bit_cast(f16x2_t, and_or(w8, 0x00F000F0u, magic_hi));   // q3, q7
+  // all eight products first, then the packs: a pack reading the product
+  // written just before it would wait a cycle (a hazard no-op)
+  const float f0 = __builtin_fmaf((float)r0[0], g.s, g.c0), f1 = __builtin_fmaf((float)r1[0], g.s, g.c1);
+  const float f2 = __builtin_fmaf((float)r2[0], g.s, g.c0), f3 = __builtin_fmaf((float)r3[0], g.s, g.c1);
+  const float f4 = __builtin_fmaf((float)r0[1], g.s, g.c0), f5 = __builtin_fmaf((float)r1[1], g.s, g.c1);
+  const float f6 = __builtin_fmaf((float)r2[1], g.s, g.c0), f7 = __builtin_fmaf((float)r3[1], g.s, g.c1);
   u32x4_t r;
-  r[0] = pack_bf16x2(__builtin_fmaf((float)r0[0], g.s, g.c0), __builtin_fmaf((float)r1[0], g.s, g.c1));
-  r[1] = pack_bf16x2(__builtin_fmaf((float)r2[0], g.s, g.c0), __builtin_fmaf((float)r3[0], g.s, g.c1));
-  r[2] = pack_bf16x2(__builtin_fmaf((float)r0[1], g.s, g.c0), __builtin_fmaf((float)r1[1], g.s, g.c1));
-  r[3] = pack_bf16x2(__builtin_fmaf((float)r2[1], g.s, g.c0), __builtin_fmaf((float)r3[1], g.s, g.c1));
+  r[0] = pack_bf16x2(f0, f1);
+  r[1] = pack_bf16x2(f2, f3);
+  r[2] = pack_bf16x2(f4, f5);
+  r[3] = pack_bf16x2(f6, f7);
   return r;
 }
 
