@@ -435,9 +435,10 @@ moe_status_t check_topk(const moe_weights_t* h, int T, int topk) {
   return MOE_OK;
 }
 
-// Workspace carving: the BF16 intermediate a, the weighted FP32 rows w*y of
-// the second GEMM (one per flat routed row, summed by the combine), the
-// contiguous layout's row-validity map, and the indexed layout's own routing.
+// Workspace carving: the BF16 intermediate a, the weighted rows w*y of the
+// second GEMM as 16-bit integers (one per flat routed row, summed by the
+// combine), the contiguous layout's row-validity map, and the indexed
+// layout's own routing.
 // Features per weighted row in the workspace: H rounded up to whole 64-feature
 // blocks (the lane-contiguous order of store_y16 permutes within a block).
 size_t yrow_ld(const moe_weights_t* h) { return ((size_t)h->desc.hidden + 63) / 64 * 64; }

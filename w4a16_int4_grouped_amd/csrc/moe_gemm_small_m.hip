@@ -30,9 +30,10 @@
 //
 // Epilogues: SwiGLU into the BF16 intermediate (W13, gate/up tiles
 // interleaved so both halves of a column sit in the same lane and register),
-// the routing-weighted FP32 row w*y stored at its flat index for the combine
-// kernel (W2, indexed / contiguous with row_src), or a BF16 store (W2,
-// masked / contiguous without row_src).
+// the routing-weighted row w*y stored at its flat index for the combine
+// kernel as 16-bit integers with a scale per 8 features (store_y16; W2,
+// indexed / contiguous with row_src), or a BF16 store (W2, masked /
+// contiguous without row_src).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -527,7 +528,7 @@ __device__ __forceinline__ void job_epi_ids(const GemmParams& p, const Job& b, i
 
 // Epilogue of one job from its prefetched routing data: pad slots and rows
 // past the set are skipped; SwiGLU and BF16 stores go to the row's slot,
-// weighted FP32 rows to its flat index.
+// weighted 16-bit rows (store_y16) to its flat index.
 template <int NT, int SET, int EPI>
 __device__ __forceinline__ void job_epilogue(const GemmParams& p, const f32x4_t (&acc)[kMT][NT],
                                              const Job& b, const int (&fid)[NT], int lane) {
