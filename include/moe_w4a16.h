@@ -272,7 +272,7 @@ moe_status_t moe_permute(const moe_weights_t* h, const uint16_t* x, int32_t T, i
  * ignored otherwise: the workspace then holds T*topk rows of H, the
  * routing-weighted outputs of the second GEMM that the combine sums, kept as
  * 16-bit integers with a power-of-two scale per 8 features, the scale's
- * exponent carried in their lowest bits (2 bytes a feature, each value within
+ * exponent carried in their top bits (2 bytes a feature, each value within
  * 2^-14 of its group's largest magnitude).
  * ovr: the indexed call's overrides (they set the alignment block and so
  * the routing capacity), NULL otherwise. */

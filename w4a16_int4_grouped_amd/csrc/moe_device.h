@@ -206,12 +206,13 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 }
 
 // Weighted rows w*y of the second GEMM, kept for the combine as 16-bit
-// integers with one power-of-two scale per 8 adjacent positions, the scale's
-// exponent carried in the values' lowest bits. For a group of 8 values v
-// with max|v| * (1 + 2^-13) < 2^e (e from frexp, clamped to >= -100), value
-// i is n_i = round_to_nearest_even(v_i * 2^(14 - e)), |n_i| < 16383, stored as
-// 2 n_i + b_i, where b_0 .. b_7 are the bits of the byte e + 128 (dword j of
-// the group holds values 2j and 2j + 1 and exponent bits j and j + 4). Read
+// words with one power-of-two scale per 8 adjacent positions, the scale's
+// exponent carried in the words' top bits. For a group of 8 values v with
+// max|v| * (1 + 2^-13) < 2^e (e from frexp, clamped to >= -100), value i is
+// n_i = round_to_nearest_even(v_i * 2^(14 - e)), |n_i| < 16383, stored as a
+// 15-bit two's complement integer in bits 0..14 with bit 15 = b_i, where
+// b_0 .. b_7 are the bits of the byte e + 128 (dword j of the group holds
+// values 2j and 2j + 1 and exponent bits j and j + 4). Read
 // back, n_i * 2^(e - 14) is within 2^-15 * 2^e <= 2^-14 * max|v| of v_i. The
 // layer's output is a BF16 sum of a token's top-k rows, rounded at 2^-9 of
 // its magnitude, so the error stays four orders of magnitude below the
@@ -248,7 +249,7 @@ __device__ __forceinline__ void store_y16(uint16_t* __restrict__ yq, size_t idx,
     const int e = max(__builtin_amdgcn_frexp_expf(amax * fabsf(w) * kExpGuard), -100);
     const float sc = __builtin_amdgcn_ldexpf(w, 14 - e);   // exact: a power-of-two multiple of w
     const uint32_t eb = (uint32_t)(e + 128);
-    const uint32_t sp = eb | (eb << 12);                    // bit j at 0, bit j + 4 at 16, after >> j
+    const uint32_t sp = (eb << 12) | (eb << 24);            // bit j at 15, bit j + 4 at 31, after << (3 - j)
 #pragma unroll
     for (int g = 2 * k; g < 2 * k + 2; ++g) {
       uint32_t x[4];
@@ -257,10 +258,11 @@ __device__ __forceinline__ void store_y16(uint16_t* __restrict__ yq, size_t idx,
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int j = 2 * (g - 2 * k) + jj;   // dword of the group
-        // low halves of the two values (the rounded integers, two's complement)
+        // low halves of the two values (the rounded integers, two's complement:
+        // bits 14 and 15 both hold the sign), bit 15 of each replaced
         const uint32_t pair = __builtin_amdgcn_perm(x[2 * jj + 1], x[2 * jj], 0x05040100u);
-        const uint32_t bits = sp >> j;
-        d[2 * g + jj] = (bits & 0x00010001u) | ((pair << 1) & ~0x00010001u);
+        const uint32_t bits = sp << (3 - j);
+        d[2 * g + jj] = (bits & 0x80008000u) | (pair & 0x7FFF7FFFu);
       }
     }
   }
@@ -270,18 +272,18 @@ __device__ __forceinline__ void store_y16(uint16_t* __restrict__ yq, size_t idx,
 }
 
 // A group of store_y16 that adds nothing: integers 0 and exponent byte 128.
-constexpr u32x4_t kY16Zero = {0u, 0u, 0u, 0x00010000u};
+constexpr u32x4_t kY16Zero = {0u, 0u, 0u, 0x80000000u};
 
 // acc += the 8 values of a group (dwords d[0..3] as stored by store_y16).
 __device__ __forceinline__ void add_y16(f32x4_t (&acc)[2], const u32x4_t& d) {
-  const uint32_t t = (d[0] & 0x10001u) | ((d[1] & 0x10001u) << 1) | ((d[2] & 0x10001u) << 2) |
-                     ((d[3] & 0x10001u) << 3);
+  const uint32_t t = ((d[0] & 0x80008000u) >> 15) | ((d[1] & 0x80008000u) >> 14) |
+                     ((d[2] & 0x80008000u) >> 13) | ((d[3] & 0x80008000u) >> 12);
   const uint32_t eb = (t & 0xFu) | ((t >> 12) & 0xF0u);
   const float sc = __uint_as_float((eb - 128u + 127u - 14u) << 23);   // 2^(e - 14)
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const float lo = (float)((int32_t)(d[m] << 16) >> 17);
-    const float hi = (float)((int32_t)d[m] >> 17);
+    const float lo = (float)((int32_t)(d[m] << 17) >> 17);
+    const float hi = (float)((int32_t)(d[m] << 1) >> 17);
     acc[m >> 1][2 * (m & 1)] = __builtin_fmaf(lo, sc, acc[m >> 1][2 * (m & 1)]);
     acc[m >> 1][2 * (m & 1) + 1] = __builtin_fmaf(hi, sc, acc[m >> 1][2 * (m & 1) + 1]);
   }
