@@ -244,68 +244,3 @@ def test_multi_block_experts(E, H, I, T, topk, layout, with_src):
         ref = O.moe_contiguous(a, m_idx, w)
         valid = m_idx >= 0
         check_tol(O.bf16_to_f64(bits_host(out))[valid], ref[valid], "contiguous multi-block rows")
-
-
-def pair_routing(T, topk, counts, seed):
-    """ids [T, topk] with the given rows per expert (sum = T * topk, each
-    count below T) and distinct experts within a token, and routing weights:
-    flat list of experts in order, token t takes entries t, t + T, ..."""
-    flat = np.repeat(np.arange(len(counts)), counts)
-    assert flat.size == T * topk and max(counts) < T
-    ids = np.stack([flat[j * T:(j + 1) * T] for j in range(topk)], axis=1).astype(np.int32)
-    assert all(len(set(r)) == topk for r in ids)
-    g = np.random.default_rng(seed)
-    tw = g.random((T, topk)).astype(np.float32) + 0.1
-    return ids, (tw / tw.sum(axis=1, keepdims=True)).astype(np.float32)
-
-
-# rows per expert: 4 blocks (last 8 rows), 2 full, full + 1 row, 1 full,
-# 2 full + 44, full + 67 -> block pairs (2i, 2i+1) of one expert with a full
-# first block, with full and partial second blocks, and blocks left to the
-# 128-row K loop (a lone block, a pair split across two experts)
-PAIR_COUNTS = [392, 256, 129, 128, 300, 195]
-
-
-@pytest.mark.parametrize("layout,with_src", [("contiguous", True), ("contiguous", False), ("indexed", True)])
-def test_pair_tiles_match_128_row_loop(layout, with_src, monkeypatch):
-    """With MOE_W4A16_PAIR=1 (read at prepare) and experts averaging 1.5 blocks
-    or more, block pairs of one expert go to the 256-row K loop and the other
-    blocks to the 128-row K loop. Both loops accumulate the same MFMAs in the
-    same k order, so the layer matches the 128-row loop alone (the default)
-    bit for bit, and the oracle within the layer tolerance."""
-    require_gpu()
-    E, H, I, T, topk = 6, 512, 512, 700, 2
-    log(f"case pair tiles {layout} row_src={with_src} E={E} H={H} I={I} T={T} counts={PAIR_COUNTS}")
-    w = tiny_weights(E, H, I, seed=77)
-    x = synth.activations(93, T, H)
-    ids, tw = pair_routing(T, topk, PAIR_COUNTS, 94)
-    outs = []
-    for pair in ("1", "0"):
-        monkeypatch.setenv("MOE_W4A16_PAIR", pair)
-        if layout == "indexed":
-            h = prepare(w, "indexed")
-            assert "schedule=large-M block=128" in describe(h, T, topk)
-            out = h.indexed(bf16_dev(x), i32_dev(ids), f32_dev(tw))
-        else:
-            a, m_idx, row_src = O.contiguous_layout(x, ids, E, 128)
-            assert a.shape[0] == 14 * 128
-            h = prepare(w, "contiguous")
-            describe(h, a.shape[0])
-            if with_src:
-                out = h.contiguous(bf16_dev(a), i32_dev(m_idx), i32_dev(row_src), f32_dev(tw), T, topk)
-            else:
-                out = h.contiguous(bf16_dev(a), i32_dev(m_idx))
-        outs.append(bits_host(out))
-    # the row-wise store writes only the rows that hold a token
-    rows = (m_idx >= 0) if layout == "contiguous" and not with_src else slice(None)
-    assert np.array_equal(outs[0][rows], outs[1][rows]), "pair tiles differ from the 128-row K loop"
-    if layout == "indexed":
-        ref = O.moe_indexed(x, ids, tw, w, E=E)
-        check_tol(O.bf16_to_f64(outs[0]), ref, "indexed pair tiles")
-    elif with_src:
-        ref = O.moe_contiguous(a, m_idx, w, row_src=row_src, topk_w=tw, T=T, topk=topk)
-        check_tol(O.bf16_to_f64(outs[0]), ref, "contiguous pair tiles + combine")
-    else:
-        ref = O.moe_contiguous(a, m_idx, w)
-        valid = m_idx >= 0
-        check_tol(O.bf16_to_f64(outs[0])[valid], ref[valid], "contiguous pair tiles rows")

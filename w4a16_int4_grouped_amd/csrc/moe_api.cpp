@@ -64,9 +64,6 @@ struct EnvOverrides {
   int ksplit = 0;        // MOE_W4A16_KSPLIT: force the small-M split-K factor (tests)
   int validate = 0;      // MOE_W4A16_VALIDATE: synchronous checks of device-side index data
   int wide = 0;          // MOE_W4A16_WIDE: large-M K loop over 256-row tiles (two blocks of an expert)
-  // MOE_W4A16_PAIR=1: block pairs of one expert on the 256-row K loop, the
-  // other blocks on the 128-row K loop (ablation: measured slower overall)
-  int pair = 0;
   // MOE_W4A16_XCD_DEAL: large-M K loop on blocks, blocks per unit dealt
   // round-robin to the XCDs (0: each XCD one contiguous range of blocks)
   int xcd_deal = 2;
@@ -83,7 +80,6 @@ struct EnvOverrides {
     ksplit = geti("MOE_W4A16_KSPLIT");
     validate = geti("MOE_W4A16_VALIDATE");
     wide = geti("MOE_W4A16_WIDE");
-    pair = geti("MOE_W4A16_PAIR");
     xcd_deal = geti("MOE_W4A16_XCD_DEAL", 2);
   }
 };
@@ -231,24 +227,6 @@ hipError_t run_gemm(int mat, const Schedule& sc, const GemmParams& p0, int set, 
       const int G = env.xcd_deal, units = (p.nsets + G - 1) / G;
       p.xcd_deal = G;
       p.total_wg = 8 * ((units + 7) / 8) * G * p.wg_per_set;
-    }
-    // Ablation (MOE_W4A16_PAIR=1), for experts averaging 1.5 blocks or more:
-    // the block pairs of one expert whose first block is full go to the
-    // 256-row K loop (each dequantised fragment feeds twice the tokens),
-    // every other block to the 128-row K loop; both launches are timed as the
-    // one GEMM. Same box, Zipf prefill: 6281 -> 6990 us per layer.
-    if (env.pair && wide_form_fits(p, set) && p.nsets >= 2 &&
-        (set == SET_BLOCKS ? 2L * p.nsets >= 3L * p.E : sc.rows >= 192)) {
-      GemmParams pw = p;
-      const int npairs = (p.nsets + 1) / 2;
-      pw.xcd_deal = 0;
-      pw.pair_only = 1;
-      pw.total_wg = 8 * ((npairs + 7) / 8) * p.wg_per_set;
-      p.pair_skip = 1;
-      return run(mat == 13 ? "gemm_w13_large_m" : "gemm_w2_large_m", s, [&] {
-        const hipError_t e = launch_gemm_wide(pw, set, epi, s);
-        return e != hipSuccess ? e : launch_gemm_large_m(p, set, epi, s);
-      });
     }
     return run(mat == 13 ? "gemm_w13_large_m" : "gemm_w2_large_m", s,
                [&] { return launch_gemm_large_m(p, set, epi, s); });

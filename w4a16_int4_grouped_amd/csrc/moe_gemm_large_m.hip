@@ -509,13 +509,6 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m(const GemmParams p) {
     n_eff = __builtin_amdgcn_readfirstlane(wave_max(last));
   }
   if (c.count <= 0 || c.e < 0 || c.e >= p.E || n_eff <= 0) return;
-  if constexpr (KCR == 0 && (SET == SET_ROUTED || SET == SET_BLOCKS)) {
-    if (p.pair_skip) {   // the 256-row K loop computes this block
-      int nblk = p.nsets;
-      if constexpr (SET == SET_ROUTED) nblk = min(max(p.routing_hdr[HDR_TOTAL], 0) / kBM, p.nsets);
-      if (pair_taken<SET>(p, set >> 1, nblk, lane)) return;
-    }
-  }
 
   const size_t tile0 = ((size_t)c.e * p.RG + c.rg) * p.Kc;
   c.wq = reinterpret_cast<const u32x4_t*>(p.wq) + tile0 * (kMT * 64);

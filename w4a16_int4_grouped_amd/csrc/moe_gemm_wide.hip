@@ -33,9 +33,7 @@
 //
 // Row sets: routing blocks (indexed, block 128) or 128-row contiguous
 // blocks, paired as (2i, 2i+1); a pair whose blocks belong to two experts is
-// run as two 128-row tiles. With pair_only (the MOE_W4A16_PAIR ablation) it
-// computes only the pairs pair_taken accepts, and the 128-row kernel the
-// other blocks. Epilogues as in the 128-row kernel.
+// run as two 128-row tiles. Epilogues as in the 128-row kernel.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -274,6 +272,46 @@ __device__ __forceinline__ void wide_tile_any(const GemmParams& p, const WideCtx
     wide_tile<SET, EPI, 16>(p, c, lds, rows);
 }
 
+// Expert and one-past-last-row of block b (uniform over the wave; -1 / 0
+// for a block past the set, an empty block or a block of no expert).
+template <int SET>
+__device__ __forceinline__ void block_info(const GemmParams& p, int b, int nblocks, int lane, int& e,
+                                           int& n_eff) {
+  e = -1;
+  n_eff = 0;
+  if (b >= nblocks) return;
+  const int slot0 = b * kBM1;
+  if constexpr (SET == SET_ROUTED) {
+    e = p.block_expert[b];
+    int last = 0;
+#pragma unroll
+    for (int r = lane; r < kBM1; r += 64) {
+      const int f = p.sorted_ids[slot0 + r];
+      if (f >= 0 && f < p.sentinel) last = r + 1;
+    }
+    n_eff = wave_max(last);
+  } else {
+    int m[2], mx = -1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      m[i] = p.m_indices[slot0 + lane + 64 * i];
+      if (m[i] >= 0 && m[i] < p.E) mx = max(mx, m[i]);
+    }
+    e = wave_max(mx);
+    int last = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (m[i] == e && e >= 0) last = lane + 64 * i + 1;
+    n_eff = wave_max(last);
+  }
+  if (e < 0 || e >= p.E) {
+    e = -1;
+    n_eff = 0;
+  }
+  e = __builtin_amdgcn_readfirstlane(e);
+  n_eff = __builtin_amdgcn_readfirstlane(n_eff);
+}
+
 template <int SET, int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_wide(const GemmParams p) {
   __shared__ u32x4_t lds0[kStageU4], lds1[kStageU4], lds2[kStageU4], lds3[kStageU4];
@@ -289,19 +327,12 @@ __global__ __launch_bounds__(512, 1) void gemm_wide(const GemmParams p) {
         hdr[HDR_T] * hdr[HDR_TOPK] != p.sentinel)
       return;   // routing made for other shapes: compute nothing
     nblocks = min(max(hdr[HDR_TOTAL], 0) / kBM1, p.nsets);
+    logical = xcd_remap_active(blockIdx.x, (nblocks + 1) / 2 * p.wg_per_set);
+    if (logical < 0) return;
   } else {
     nblocks = p.nsets;
-  }
-  if (p.pair_only) {
-    // the pairs taken come in runs (one hot expert's blocks): dealt one pair
-    // at a time round-robin to the XCDs, they spread over all of them
-    logical = xcd_deal_blocks(blockIdx.x, (nblocks + 1) / 2, p.wg_per_set, 1);
-  } else if constexpr (SET == SET_ROUTED) {
-    logical = xcd_remap_active(blockIdx.x, (nblocks + 1) / 2 * p.wg_per_set);
-  } else {
     logical = xcd_remap(blockIdx.x, p.total_wg);
   }
-  if (logical < 0) return;
   const int pair = logical / p.wg_per_set;
   const int quad = logical - pair * p.wg_per_set;
   const int rg_raw = quad * 4 + (c.wave >> 1);
@@ -311,17 +342,15 @@ __global__ __launch_bounds__(512, 1) void gemm_wide(const GemmParams p) {
   c.rd = stage_rd(lane);
 
   int e0, n0, e1, n1;
-  pair_block_info<SET>(p, 2 * pair, nblocks, lane, e0, n0);
-  pair_block_info<SET>(p, 2 * pair + 1, nblocks, lane, e1, n1);
-  const bool taken = e0 >= 0 && e1 == e0 && n0 == kBM1 && n1 > 0;   // as pair_taken
-  if (p.pair_only && !taken) return;   // the 128-row kernel computes these blocks
+  block_info<SET>(p, 2 * pair, nblocks, lane, e0, n0);
+  block_info<SET>(p, 2 * pair + 1, nblocks, lane, e1, n1);
   auto bind = [&](int e) {
     c.e = e;
     const size_t tile0 = ((size_t)e * p.RG + c.rg) * p.Kc;
     c.wq = reinterpret_cast<const u32x4_t*>(p.wq) + tile0 * (kMT * 64) + c.mt0 * 64;
     c.ws = reinterpret_cast<const uint32_t*>(p.wsc) + tile0 * 128 + (c.mt0 >> 1);
   };
-  if (taken) {   // one 256-row tile
+  if (e0 >= 0 && e1 == e0 && n0 == kBM1 && n1 > 0) {   // one 256-row tile
     bind(e0);
     c.slot0 = 2 * pair * kBM1;
     wide_tile_any<SET, EPI>(p, c, lds, kBM1 + n1);

@@ -39,8 +39,6 @@ struct GemmParams {
   int nsets;             // row sets (experts or blocks)
   int total_wg;
   int xcd_deal;          // large-M K loop on blocks: units of xcd_deal blocks dealt round-robin to the XCDs (0: off)
-  int pair_only;         // 256-row K loop: only the block pairs pair_taken accepts, pairs dealt round-robin to the XCDs
-  int pair_skip;         // 128-row K loop: leave the block pairs pair_taken accepts (to the 256-row loop)
   // row sets
   const int32_t* counts;
   const int32_t* offsets;
@@ -88,20 +86,6 @@ inline bool src_fits_u32(const GemmParams& p, int set) {
   return rows <= 0 || (rows - 1) * p.src_ld * 2 + (int64_t)p.K * 2 <= (int64_t)0xFFFFFFFF;
 }
 
-// The 256-row K loop's requirements: the K-loop form (no resident tile), K a
-// whole number of chunk pairs, 128-row routing or contiguous blocks and a
-// token matrix under 4 GiB.
-inline bool wide_form_fits(const GemmParams& p, int set) {
-  if (set == SET_ROUTED) {
-    if (p.block != 128) return false;
-  } else if (set == SET_BLOCKS) {
-    if (p.block_rows != 128) return false;
-  } else {
-    return false;
-  }
-  return p.qpw == 0 && p.K > 0 && p.K % 256 == 0 && src_fits_u32(p, set);
-}
-
 // dispatch 1 or 2: routing blocks (SET_ROUTED, block 16*nt) only; total_wg
 // workgroups, enough that a static range spans at most 64 blocks.
 hipError_t launch_gemm_small_m(const GemmParams& p, int set, int epi, int nt, hipStream_t s);
@@ -136,8 +120,7 @@ hipError_t launch_dequant_expert(const MatLayout& m, const char* prepared, int e
                                  uint16_t* out, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t s);
 // Large-M K loop over 256-row tiles (pairs of 128-row routing or contiguous
-// blocks of one expert); p.total_wg = ceil(nsets / 2) * wg_per_set, or with
-// pair_only 8 * ceil(ceil(nsets / 2) / 8) * wg_per_set.
+// blocks of one expert); p.total_wg = ceil(nsets / 2) * wg_per_set.
 hipError_t launch_gemm_wide(const GemmParams& p, int set, int epi, hipStream_t s);
 // Data checks (MOE_W4A16_VALIDATE=1); each adds its count to *bad.
 // Entries of v[0, n) outside [lo, hi):

@@ -13,7 +13,6 @@
 #include <hip/hip_runtime.h>
 
 #include "moe_device.h"
-#include "moe_launch.h"
 #include "moe_layout.h"
 
 namespace moe {
@@ -49,63 +48,6 @@ __device__ __forceinline__ void dma_tile(u32x4_t* lds_buf, const char* src0, con
       __builtin_amdgcn_global_load_lds(src + s * 64, (lds_void_t*)dst, 16, 0, 0);
     }
   }
-}
-
-// ---- Block pairs. The 256-row K loop (moe_gemm_wide.hip) takes the pairs
-// of 128-row blocks (2i, 2i + 1) that belong to one expert and whose first
-// block is full; with pair_only / pair_skip set, the 128-row kernel computes
-// every other block. Both evaluate this one predicate, so every block is
-// computed exactly once.
-
-// Expert of 128-row block b and one past its last valid row (uniform over
-// the wave; -1 / 0 for a block past the set, an empty block or a block of no
-// expert). A block's valid rows come first, so n_eff counts them.
-template <int SET>
-__device__ __forceinline__ void pair_block_info(const GemmParams& p, int b, int nblocks, int lane, int& e,
-                                                int& n_eff) {
-  e = -1;
-  n_eff = 0;
-  if (b >= nblocks) return;
-  const int slot0 = b * 128;
-  if constexpr (SET == SET_ROUTED) {
-    e = p.block_expert[b];
-    int last = 0;
-#pragma unroll
-    for (int r = lane; r < 128; r += 64) {
-      const int f = p.sorted_ids[slot0 + r];
-      if (f >= 0 && f < p.sentinel) last = r + 1;
-    }
-    n_eff = wave_max(last);
-  } else {
-    int m[2], mx = -1;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      m[i] = p.m_indices[slot0 + lane + 64 * i];
-      if (m[i] >= 0 && m[i] < p.E) mx = max(mx, m[i]);
-    }
-    e = wave_max(mx);
-    int last = 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (m[i] == e && e >= 0) last = lane + 64 * i + 1;
-    n_eff = wave_max(last);
-  }
-  if (e < 0 || e >= p.E || n_eff <= 0) {
-    e = -1;
-    n_eff = 0;
-  }
-  e = __builtin_amdgcn_readfirstlane(e);
-  n_eff = __builtin_amdgcn_readfirstlane(n_eff);
-}
-
-// Whether pair i is a 256-row tile: both blocks of one expert, the first
-// full.
-template <int SET>
-__device__ __forceinline__ bool pair_taken(const GemmParams& p, int i, int nblocks, int lane) {
-  int e0, n0, e1, n1;
-  pair_block_info<SET>(p, 2 * i, nblocks, lane, e0, n0);
-  pair_block_info<SET>(p, 2 * i + 1, nblocks, lane, e1, n1);
-  return e0 >= 0 && e1 == e0 && n0 == 128 && n1 > 0;
 }
 
 // ---- Half-chunk stages (the K loops that stream the token tile through a
