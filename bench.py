@@ -248,10 +248,16 @@ def setup_case(wl, dev_w, args, torch, np, M):
             synth.scaled(wl, I=32))], mode="indexed")   # align + permute only need E and H
         ovr = {"block_m": 128}
         routing = hi.align(ids_d, ovr=ovr)
-        a_d, m_d, src_d = hi.permute(x_d, wl.topk, routing, ovr=ovr)
+        perm = hi.permute(x_d, wl.topk, routing, ovr=ovr)
         total = int(routing[7].item())
-        a_d, m_d, src_d = a_d[:total].contiguous(), m_d[:total].contiguous(), src_d[:total].contiguous()
-        del hi, routing
+        a_d, m_d, src_d = (v[:total].contiguous() for v in perm)
+
+        def route_step():
+            # the routing step that makes this input, timed on its own: it
+            # writes its own buffers, not the GEMMs' copies above
+            hi.align(ids_d, ovr=ovr, routing=routing, stream=stream)
+            hi.permute(x_d, wl.topk, routing, ovr=ovr, stream=stream, out=perm)
+        c.route_step = route_step
         out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
         ws = torch.empty(h.workspace_bytes(total, wl.topk, wl.T), dtype=torch.uint8, device="cuda")
         c.describe = f"M_pad={total}; " + h.describe(total)
@@ -484,6 +490,8 @@ def run_one(idx, w, dev_w, args, torch, np, M, with_cpu):
     rec["host_us_per_call"] = float(np.median(t["host_us"])) if t["host_us"] else None
     if args.cold_calls > 0:
         rec["per_call_flushed_us"] = cold_calls(c.step, c.stream, args.cold_calls)
+    if getattr(c, "route_step", None) is not None:
+        rec["routing_step"] = time_route(c, args, torch, M)
     rec["inputs_sha256"] = inputs_sha256(list(w) + c.inputs)
     if with_cpu and c.out is not None:
         # the GPU rows of the sample are read now; the oracle runs after every
@@ -499,6 +507,33 @@ def run_one(idx, w, dev_w, args, torch, np, M, with_cpu):
         rec["_cpu"] = (data, kind, sel, got)
     del c
     return rec
+
+
+def time_route(c, args, torch, M):
+    """The align + permute that produce the contiguous input, timed apart from
+    the layer call (which takes that input ready-made): warmup, then K calls
+    between two stream events, and the per-kernel durations of K more."""
+    for _ in range(max(args.warmup, 3)):
+        c.route_step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(c.stream)
+    for _ in range(args.steps):
+        c.route_step()
+    e1.record(c.stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    M.profile_reset()
+    M.profile_enable(True)
+    for _ in range(args.steps):
+        c.route_step()
+    torch.cuda.synchronize()
+    M.profile_enable(False)
+    kernels = {k: v[1] / v[0] * 1e3 for k, v in M.profile_read().items()}
+    log(f"  {c.wl.name} routing step (align + permute): {us:.1f} us/call; " +
+        ", ".join(f"{k}={v:.1f}" for k, v in sorted(kernels.items())))
+    return {"what": "align (128-row blocks) + permute of the T x topk rows, outside us_per_call",
+            "us_per_call": us, "kernels_avg_us": kernels}
 
 
 def cold_calls(step, stream, n):

@@ -250,13 +250,18 @@ moe_status_t moe_align_ep(const moe_weights_t* h, const int32_t* topk_ids, int32
                           const moe_tuning_t* ovr, void* routing, size_t routing_bytes,
                           moe_stream_t stream);
 
-/* Gather x rows into the aligned order (the contiguous layout's producer):
+/* Gather x rows into the aligned order (the contiguous layout's producer;
+ * Chord page, "Grouped SM90 kernels", Fig. 3):
  *   a_out      device bf16 [cap, H]: row p = x[sorted_ids[p] / topk], zero
- *              for sentinel slots
+ *              for sentinel slots below the routing's padded total (header
+ *              word 7, the layout's M_pad); rows at or past the total are
+ *              not written
  *   m_indices  device int32 [cap]: expert of row p, -1 for sentinel slots
  *   row_src    device int32 [cap]: sorted_ids[p], -1 for sentinel slots
  * Any of the three outputs may be NULL. routing must come from moe_align
- * with the same (T, topk, ovr). */
+ * with the same (T, topk, ovr); slots it names outside [0, cap) are not
+ * written. Errors: INVALID_ARG (NULL routing, NULL x with a_out and T > 0,
+ * x or a_out not 16-byte aligned, bad T / topk), MODE_MISMATCH, HIP. */
 moe_status_t moe_permute(const moe_weights_t* h, const uint16_t* x, int32_t T, int32_t topk,
                          const moe_tuning_t* ovr, const void* routing, uint16_t* a_out,
                          int32_t* m_indices, int32_t* row_src, moe_stream_t stream);

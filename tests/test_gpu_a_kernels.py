@@ -165,11 +165,44 @@ def test_permute_bit_exact(handles, block_m):
     routing = h.align(i32_dev(ids), ovr=ovr)
     a, m_idx, row_src = h.permute(bf16_dev(x), topk, routing, ovr=ovr)
     al = O.align(ids, E, block_m)
-    assert np.array_equal(bits_host(a), O.permute(x, al, topk))
+    # rows of a past the padded total lie outside the layout and are not written
+    n = al["total"]
+    assert int(routing[7].item()) == n
+    assert np.array_equal(bits_host(a)[:n], O.permute(x, al, topk)[:n])
     ok = al["sorted_ids"] < al["sentinel"]
     m_ref = np.where(ok, np.repeat(al["block_expert"], block_m)[:al["cap"]], -1)
     assert np.array_equal(m_idx.cpu().numpy(), m_ref)
     assert np.array_equal(row_src.cpu().numpy(), np.where(ok, al["sorted_ids"], -1))
+
+
+def test_permute_into_given_buffers(handles):
+    """permute() into caller-given buffers (as the bench's routing step
+    reuses them call after call) writes what a fresh call returns, twice in
+    a row, and refuses buffers smaller than the routing's capacity."""
+    import torch
+    import w4a16_int4_grouped_amd as M
+    E, T, topk = 7, 300, 3
+    h = handles(E)
+    ovr = {"block_m": 128}
+    x = bf16_dev(synth.activations(9, T, 64))
+    ids = i32_dev(routing_ids(E, T, topk, "softmax", 5))
+    routing = h.align(ids, ovr=ovr)
+    ref = [v.cpu() for v in h.permute(x, topk, routing, ovr=ovr)]
+    cap, n = ref[0].shape[0], int(routing[7].item())
+    assert 0 < n < cap
+    bufs = (torch.full((cap, 64), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16),
+            torch.full((cap,), 12345, dtype=torch.int32, device="cuda"),
+            torch.full((cap,), 12345, dtype=torch.int32, device="cuda"))
+    for _ in range(2):
+        got = h.permute(x, topk, h.align(ids, ovr=ovr, routing=routing), ovr=ovr, out=bufs)
+        assert all(g is b for g, b in zip(got, bufs))
+        a = got[0].cpu().view(torch.int16)
+        assert torch.equal(a[:n], ref[0].view(torch.int16)[:n])
+        assert bool((a[n:] == -1).all()), "rows past the padded total must stay unwritten"
+        assert torch.equal(got[1].cpu(), ref[1]) and torch.equal(got[2].cpu(), ref[2])
+    short = (bufs[0][:cap - 1], bufs[1], bufs[2])
+    with pytest.raises(M.MoeError, match="INVALID_ARG"):
+        h.permute(x, topk, routing, ovr=ovr, out=short)
 
 
 def test_dequant_exhaustive_all_scales():

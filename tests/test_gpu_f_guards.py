@@ -111,6 +111,17 @@ def test_permute_guards():
     assert np.array_equal(bits_host(a)[:n], ref_a)
     assert np.array_equal(m.cpu().numpy().reshape(-1)[:n], ref_m)
     assert np.array_equal(src.cpu().numpy().reshape(-1)[:n], ref_src)
+    # without a_out (x may then be NULL): only the two index arrays, the same
+    m.fill_(7)
+    src.fill_(7)
+    M.check(M.lib().moe_permute(h.handle, None, T, topk, M._tuning(ovr), ctypes.c_void_p(routing.data_ptr()),
+                                None, ctypes.c_void_p(m.data_ptr()), ctypes.c_void_p(src.data_ptr()), None))
+    torch.cuda.synchronize()
+    for name, wh in (("m_indices", mwhole), ("row_src", swhole)):
+        assert canary_intact(wh), f"permute wrote past {name}"
+    assert np.array_equal(m.cpu().numpy().reshape(-1)[:n], ref_m)
+    assert np.array_equal(src.cpu().numpy().reshape(-1)[:n], ref_src)
+    assert bool((m.reshape(-1)[n:] == -1).all()) and bool((src.reshape(-1)[n:] == -1).all())
 
 
 @pytest.mark.parametrize("with_src", [True, False])

@@ -234,13 +234,23 @@ class PreparedWeights:
                                  _stream(stream)))
         return routing
 
-    def permute(self, x, topk, routing, ovr=None, stream=None):
+    def permute(self, x, topk, routing, ovr=None, stream=None, out=None):
+        """Contiguous rows, m_indices and row_src of the routing; `out` may
+        give the three buffers (routing capacity rows each)."""
         import torch
         T = x.shape[0]
         L = self.routing_layout(T, topk, ovr)
-        a = torch.empty((L.cap, self.H), dtype=torch.bfloat16, device=self.device)
-        m = torch.empty(L.cap, dtype=torch.int32, device=self.device)
-        r = torch.empty(L.cap, dtype=torch.int32, device=self.device)
+        if out is None:
+            a = torch.empty((L.cap, self.H), dtype=torch.bfloat16, device=self.device)
+            m = torch.empty(L.cap, dtype=torch.int32, device=self.device)
+            r = torch.empty(L.cap, dtype=torch.int32, device=self.device)
+        else:
+            a, m, r = out
+            if (a.dtype != torch.bfloat16 or m.dtype != torch.int32 or r.dtype != torch.int32
+                    or not (a.is_contiguous() and m.is_contiguous() and r.is_contiguous())
+                    or a.dim() != 2 or a.shape[0] < L.cap or a.shape[1] != self.H
+                    or m.numel() < L.cap or r.numel() < L.cap):
+                check(MOE_ERR_INVALID_ARG)
         check(lib().moe_permute(self.handle, _ptr(x), T, topk, _tuning(ovr), _ptr(routing), _ptr(a), _ptr(m),
                                 _ptr(r), _stream(stream)))
         return a, m, r

@@ -300,29 +300,97 @@ __global__ __launch_bounds__(NWAVES * 64) void align_scatter(const int32_t* __re
                      routing + off_slot_of);
 }
 
-__global__ __launch_bounds__(256) void permute_rows(const uint16_t* __restrict__ x, int topk, int H,
-                                                    int B, int sentinel,
+// The row gather, one launch with two kinds of workgroups, dealt
+// alternately (token, slot, token, ...) so that both kinds run together
+// from start to end.
+//  - Token workgroups: one wave per token reads the token's row once and
+//    writes it to the slot of each of its routed rows (slot_of), so each x
+//    row crosses HBM once.
+//  - Slot workgroups: 64 slots each. Wave 0 writes m_indices and row_src of
+//    the 64; the padding slots among them below the routing's padded total
+//    get a zero row in a_out, wave w zeroing padding rows w, w + 4, ... so
+//    that a slot workgroup's rows are spread over its four waves.
+// Slots at or past the padded total are outside the contiguous layout:
+// a_out is not written there. a_out rows are written with nontemporal
+// stores (nothing here reads them back). Every slot read from the routing
+// is checked against the capacity before it is written to.
+constexpr int kPermutePieces = 4;   // 1 KB pieces of a row a wave holds at once
+
+__global__ __launch_bounds__(256) void permute_rows(const uint16_t* __restrict__ x, int T, int topk, int H,
+                                                    int B, int sentinel, int cap, int ntok_wg,
+                                                    int nslot_wg, const int32_t* __restrict__ hdr,
                                                     const int32_t* __restrict__ sorted_ids,
+                                                    const int32_t* __restrict__ slot_of,
                                                     const int32_t* __restrict__ block_expert,
                                                     uint16_t* __restrict__ a_out,
                                                     int32_t* __restrict__ m_indices,
                                                     int32_t* __restrict__ row_src) {
-  const int p = blockIdx.x;
-  const int f = sorted_ids[p];
-  const bool valid = f >= 0 && f < sentinel;
-  if (a_out) {
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(a_out + (size_t)p * H);
-    if (valid) {   // uniform over the workgroup
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)(f / topk) * H);
-      for (int c = threadIdx.x; c < H / 8; c += 256) dst[c] = src[c];
-    } else {
-      const u32x4_t z = {0u, 0u, 0u, 0u};
-      for (int c = threadIdx.x; c < H / 8; c += 256) dst[c] = z;
-    }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H8 = H / 8;   // 16-byte pieces of a row
+  // workgroup i: while both kinds last, even i the token workgroup i/2 and
+  // odd i the slot workgroup i/2; then the rest of the larger kind
+  const int i = (int)blockIdx.x, both = min(ntok_wg, nslot_wg);
+  bool token_wg;
+  int idx;
+  if (i < 2 * both) {
+    token_wg = !(i & 1);
+    idx = i >> 1;
+  } else {
+    token_wg = ntok_wg > nslot_wg;
+    idx = i - both;
   }
-  if (threadIdx.x == 0) {
-    if (m_indices) m_indices[p] = valid ? block_expert[p / B] : -1;
-    if (row_src) row_src[p] = valid ? f : -1;
+  if (token_wg) {
+    const int t = idx * 4 + wave;
+    if (t >= T) return;
+    int my_slot = -1;   // lane j < topk: the slot of row (t, j), -1 if dropped
+    if (lane < topk) {
+      const int q = slot_of[(size_t)t * topk + lane];
+      my_slot = (q >= 0 && q < cap) ? q : -1;
+    }
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (size_t)t * H);
+    for (int c0 = 0; c0 < H8; c0 += 64 * kPermutePieces) {
+      u32x4_t v[kPermutePieces];
+#pragma unroll
+      for (int u = 0; u < kPermutePieces; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < H8) v[u] = src[c];
+      }
+      for (int j = 0; j < topk; ++j) {
+        const int q = __builtin_amdgcn_readlane(my_slot, j);
+        if (q < 0) continue;
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(a_out + (size_t)q * H);
+#pragma unroll
+        for (int u = 0; u < kPermutePieces; ++u) {
+          const int c = c0 + u * 64 + lane;
+          if (c < H8) __builtin_nontemporal_store(v[u], dst + c);
+        }
+      }
+    }
+    return;
+  }
+  const int base = idx * 64;   // this workgroup's first slot
+  const int p = base + lane;
+  bool pad = false;
+  if (p < cap) {
+    const int f = sorted_ids[p];
+    const bool valid = f >= 0 && f < sentinel;
+    if (wave == 0) {
+      if (m_indices) m_indices[p] = valid ? block_expert[p / B] : -1;
+      if (row_src) row_src[p] = valid ? f : -1;
+    }
+    pad = !valid;
+  }
+  if (!a_out) return;   // uniform: a kernel argument
+  const int total = min(max(hdr[HDR_TOTAL], 0), cap);
+  uint64_t pads = __ballot(pad && p < total);
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  for (int k = 0; pads; ++k) {
+    const int l = __builtin_ctzll(pads);
+    pads &= pads - 1;
+    if ((k & 3) != wave) continue;
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(a_out + (size_t)(base + l) * H);
+    for (int c = lane; c < H8; c += 64) __builtin_nontemporal_store(z, dst + c);
   }
 }
 
@@ -365,9 +433,11 @@ hipError_t launch_permute(const uint16_t* x, int T, int topk, int H, const Routi
                           const int32_t* routing, uint16_t* a_out, int32_t* m_indices,
                           int32_t* row_src, hipStream_t s) {
   if (L.cap == 0) return hipSuccess;
-  hipLaunchKernelGGL(permute_rows, dim3(L.cap), dim3(256), 0, s, x, topk, H, L.block, T * topk,
-                     routing + L.off_sorted, routing + L.off_block_expert, a_out, m_indices,
-                     row_src);
+  const int ntok_wg = a_out ? (T + 3) / 4 : 0;
+  const int nslot_wg = (L.cap + 63) / 64;
+  hipLaunchKernelGGL(permute_rows, dim3(ntok_wg + nslot_wg), dim3(256), 0, s, x, T, topk, H, L.block,
+                     T * topk, L.cap, ntok_wg, nslot_wg, routing + L.off_header, routing + L.off_sorted,
+                     routing + L.off_slot_of, routing + L.off_block_expert, a_out, m_indices, row_src);
   return hipGetLastError();
 }
 
