@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kCountThreads = 256;
 constexpr int kScanThreads = 1024;
+constexpr int kScanLoads = 32;   // chunk counts an expert's thread loads at once in the scan
 // One-workgroup path limits. Above 4096 rows the multi-workgroup path is
 // faster (the one-workgroup path places 1024 rows per round, about 1.7 us
 // each).
@@ -125,17 +126,19 @@ __device__ void scan_experts(int32_t* padded, int32_t* offsets, int E) {
 }
 
 // Sentinels, the block -> expert map and the header. Every slot of
-// sorted_ids gets the sentinel (coalesced, all threads); placement, which
-// runs after a barrier or in a later kernel, overwrites the slots that hold
-// rows. start[0..E] holds the scanned offsets. (The placement also writes
+// sorted_ids gets the sentinel (coalesced, all threads; skipped when a
+// many-workgroup kernel before this one wrote them); placement, which runs
+// after a barrier or in a later kernel, overwrites the slots that hold rows.
+// start[0..E] holds the scanned offsets. (The placement also writes
 // slot_of[f], the slot of flat row f or -1 for a dropped row, which the
 // combine reads.)
 __device__ void fill_padding(int32_t* routing, const int32_t* start, int E, int B, int T, int topk,
                              int cap, int nblocks, int nchunks, int32_t* sorted_ids,
-                             int32_t* block_expert) {
+                             int32_t* block_expert, bool fill_sentinels) {
   const int sentinel = T * topk;
   const int total = start[E];
-  for (int q = threadIdx.x; q < cap; q += blockDim.x) sorted_ids[q] = sentinel;
+  if (fill_sentinels)
+    for (int q = threadIdx.x; q < cap; q += blockDim.x) sorted_ids[q] = sentinel;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const int s0 = start[e], s1 = start[e + 1];
     for (int b = s0 / B; b < s1 / B; ++b) block_expert[b] = e;
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(1024) void align_small(const int32_t* __restrict__ 
   __syncthreads();
   scan_experts(start, routing + off_offsets, E);
   __syncthreads();
-  fill_padding(routing, start, E, B, T, topk, cap, nblocks, 0, sorted_ids, routing + off_be);
+  fill_padding(routing, start, E, B, T, topk, cap, nblocks, 0, sorted_ids, routing + off_be, true);
   for (int e = threadIdx.x; e < E; e += 1024) {
     counts[e] = hist[e];
     hist[e] = start[e];   // next free slot
@@ -228,11 +231,17 @@ __global__ __launch_bounds__(1024) void align_small(const int32_t* __restrict__ 
 }
 
 // ---- large path ------------------------------------------------------------
+// Per-chunk expert counts. The chunk workgroups also write the sentinel
+// into every slot of sorted_ids (cap of them), which the one-workgroup scan
+// would otherwise write alone.
 __global__ __launch_bounds__(kCountThreads) void align_count(const int32_t* __restrict__ ids,
                                                              const int32_t* __restrict__ map, int Eg,
                                                              int n, int E,
-                                                             int32_t* __restrict__ chunk_hist) {
+                                                             int32_t* __restrict__ chunk_hist,
+                                                             int32_t* __restrict__ sorted_ids, int cap) {
   extern __shared__ int32_t hist[];
+  for (int q = blockIdx.x * kCountThreads + threadIdx.x; q < cap; q += gridDim.x * kCountThreads)
+    sorted_ids[q] = n;   // the sentinel T * topk
   for (int i = threadIdx.x; i < E; i += kCountThreads) hist[i] = 0;
   __syncthreads();
   const int base = blockIdx.x * kAlignChunk;
@@ -260,12 +269,13 @@ __global__ __launch_bounds__(kScanThreads) void align_scan(int32_t* __restrict__
   // per expert: exclusive prefix over chunks (in place) and the total
   for (int e = threadIdx.x; e < E; e += kScanThreads) {
     int run = 0;
-    for (int c0 = 0; c0 < nchunks; c0 += 8) {   // 8 independent loads in flight
-      int h[8];
+    for (int c0 = 0; c0 < nchunks; c0 += kScanLoads) {   // kScanLoads independent loads in flight
+      int h[kScanLoads];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h[i] = c0 + i < nchunks ? chunk_hist[(size_t)(c0 + i) * E + e] : 0;
+      for (int i = 0; i < kScanLoads; ++i)
+        h[i] = c0 + i < nchunks ? chunk_hist[(size_t)(c0 + i) * E + e] : 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < kScanLoads; ++i) {
         if (c0 + i < nchunks) chunk_hist[(size_t)(c0 + i) * E + e] = run;
         run += h[i];
       }
@@ -277,7 +287,7 @@ __global__ __launch_bounds__(kScanThreads) void align_scan(int32_t* __restrict__
   scan_experts(padded, routing + off_offsets, E);
   __syncthreads();
   fill_padding(routing, padded, E, B, T, topk, cap, nblocks, nchunks, routing + off_sorted,
-               routing + off_be);
+               routing + off_be, nchunks == 0);   // align_count wrote them when it ran
 }
 
 template <int NWAVES>
@@ -410,8 +420,7 @@ hipError_t launch_align(const int32_t* topk_ids, int T, int topk, int E, const R
   const size_t lds_e = (size_t)E * sizeof(int32_t);
   if (L.nchunks > 0) {
     hipLaunchKernelGGL(align_count, dim3(L.nchunks), dim3(kCountThreads), lds_e, s, topk_ids, map, Eg,
-                       n, E,
-                       routing + L.off_scratch);
+                       n, E, routing + L.off_scratch, routing + L.off_sorted, L.cap);
   }
   hipLaunchKernelGGL(align_scan, dim3(1), dim3(kScanThreads), lds_e + sizeof(int32_t), s, routing,
                      E, L.block, T, topk, L.nchunks, L.cap, L.nblocks, L.off_counts, L.off_offsets,
