@@ -75,6 +75,9 @@ def parse():
     ap.add_argument("--cold-calls", type=int, default=0, metavar="N",
                     help="after the timed steps, time N more calls one by one, each after a 1 GiB write "
                          "that evicts the L2s and the MALL, and report their p10/p50/p90")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one call of each workload in a HIP graph (on a stream of its own) "
+                         "and time K replays: the layer without host launch overhead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (steps times), the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -175,7 +178,9 @@ def setup_case(wl, dev_w, args, torch, np, M):
     c.wl = wl
     c.h = M.PreparedWeights(*dev_w, mode=wl.layout)
     h = c.h
-    stream = torch.cuda.current_stream()
+    # a graph is captured on a stream of the caller's own (not the null stream);
+    # without --graph the calls run on torch's current stream
+    stream = torch.cuda.Stream() if args.graph else torch.cuda.current_stream()
     c.stream = stream
     c.inputs = []
     if wl.layout == "indexed":
@@ -283,6 +288,8 @@ def setup_case(wl, dev_w, args, torch, np, M):
         def step():
             h.masked(a3_d, mm_d, wl.expected_m, out=out, ws=ws, stream=stream)
     c.step = step
+    if args.graph:
+        torch.cuda.synchronize()   # inputs written on torch's stream before the calls on c.stream
     return c
 
 
@@ -492,6 +499,8 @@ def run_one(idx, w, dev_w, args, torch, np, M, with_cpu):
         rec["per_call_flushed_us"] = cold_calls(c.step, c.stream, args.cold_calls)
     if getattr(c, "route_step", None) is not None:
         rec["routing_step"] = time_route(c, args, torch, M)
+    if args.graph:
+        rec["graph_replay"] = time_graph(c, args, torch)
     rec["inputs_sha256"] = inputs_sha256(list(w) + c.inputs)
     if with_cpu and c.out is not None:
         # the GPU rows of the sample are read now; the oracle runs after every
@@ -507,6 +516,32 @@ def run_one(idx, w, dev_w, args, torch, np, M, with_cpu):
         rec["_cpu"] = (data, kind, sel, got)
     del c
     return rec
+
+
+def time_graph(c, args, torch):
+    """One call captured in a HIP graph on the workload's stream (inputs,
+    output and workspace are the step's fixed buffers), then K replays
+    between two events on that stream. Returns µs per replayed call."""
+    c.step()   # warm (already warm after the timed steps)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=c.stream):
+        c.step()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(c.stream):
+        for _ in range(max(args.warmup, 3)):
+            g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(c.stream)
+    with torch.cuda.stream(c.stream):
+        for _ in range(args.steps):
+            g.replay()
+    e1.record(c.stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    log(f"  {c.wl.name} graph replay: {us:.1f} us/call")
+    return {"us_per_call": us, "replays": args.steps}
 
 
 def time_route(c, args, torch, M):
@@ -645,6 +680,8 @@ def main():
         result["config"][k] = h[k]
     if "per_call_flushed_us" in h:
         result["per_call_flushed_us"] = h["per_call_flushed_us"]
+    if "graph_replay" in h:
+        result["graph_replay"] = h["graph_replay"]
     if "cpu_baseline" in h:
         result["cpu_baseline"] = h["cpu_baseline"]
     if "parity" in h:
