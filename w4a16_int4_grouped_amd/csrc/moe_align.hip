@@ -15,9 +15,10 @@
 //   small (decode-sized routings, up to 4096 rows): one workgroup of 16
 //     waves counts, scans, fills the padding and places every row in a
 //     single launch;
-//   large: per-chunk counts, a one-workgroup scan over experts (which also
-//     turns the chunk counts into per-chunk prefixes), then one 4-wave
-//     workgroup per chunk places that chunk's rows.
+//   large: per-chunk counts (the chunk workgroups also write the sentinel
+//     into every slot), a one-workgroup scan over experts (which also turns
+//     the chunk counts into per-chunk prefixes), then one 4-wave workgroup
+//     per chunk places that chunk's rows.
 #include <hip/hip_runtime.h>
 
 #include "moe_device.h"
@@ -232,8 +233,8 @@ __global__ __launch_bounds__(1024) void align_small(const int32_t* __restrict__ 
 
 // ---- large path ------------------------------------------------------------
 // Per-chunk expert counts. The chunk workgroups also write the sentinel
-// into every slot of sorted_ids (cap of them), which the one-workgroup scan
-// would otherwise write alone.
+// into every slot of sorted_ids (cap of them), so that the one-workgroup
+// scan after them does not have to.
 __global__ __launch_bounds__(kCountThreads) void align_count(const int32_t* __restrict__ ids,
                                                              const int32_t* __restrict__ map, int Eg,
                                                              int n, int E,
