@@ -34,6 +34,7 @@ ROUTINGS = [
     ("experts-max", 4096, 700, 8, "zipf"),       # the largest expert count a handle accepts
     ("topk-max", 96, 64, 64, "softmax"),         # the largest top-k (64): 4096 rows
     ("many-rows", 384, 16384, 8, "zipf"),        # 131072 rows in 128 chunks
+    ("no-rows-chunked", 600, 0, 4, "softmax"),   # no rows above 512 experts: the scan alone writes the sentinels
 ]
 
 
