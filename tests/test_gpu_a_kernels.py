@@ -206,6 +206,26 @@ def test_permute_into_given_buffers(handles):
         h.permute(x, topk, routing, ovr=ovr, out=short)
 
 
+@pytest.mark.parametrize("E", [7, 600])
+def test_permute_empty_routing(handles, E):
+    """No tokens: every slot's m_indices and row_src become -1 and no row of
+    a_out is written (the padded total is 0), on both alignment paths."""
+    import torch
+    h = handles(E)
+    ids = i32_dev(np.zeros((0, 4), np.int32))
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    routing = h.align(ids)
+    cap = h.routing_layout(0, 4).cap
+    assert int(routing[7].item()) == 0 and cap > 0
+    bufs = (torch.full((cap, 64), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16),
+            torch.full((cap,), 12345, dtype=torch.int32, device="cuda"),
+            torch.full((cap,), 12345, dtype=torch.int32, device="cuda"))
+    a, m, r = h.permute(x, 4, routing, out=bufs)
+    torch.cuda.synchronize()
+    assert bool((m == -1).all()) and bool((r == -1).all())
+    assert bool((a.view(torch.int16) == -1).all()), "a row past the padded total was written"
+
+
 def test_dequant_exhaustive_all_scales():
     """Every finite BF16 scale below 2^117 in magnitude (plus zeros and
     subnormals) against all 16 codes, through the GEMMs' dequantisation
