@@ -68,22 +68,23 @@ __device__ __forceinline__ void load_a(AFrag& f, const u32x4_t* __restrict__ wq,
   f.S = __builtin_nontemporal_load(ws + lane);
 }
 
-template <int NT>
+template <int NA, int NT>
 __device__ __forceinline__ void load_b(u32x4_t (&st)[NT], const uint16_t* const (&lrow)[NT], int kc,
                                        int kmax, bool whole) {
-  // this thread's 16-byte piece of each token row; k past K reads zero (the
+  // this thread's 16-byte piece of each token row of the first NA tiles (a
+  // pass's tiles past its rows are neither loaded nor stored); k past K reads zero (the
   // substitute address is the row's first element, always valid). whole
   // (uniform): K is whole chunks and kc (always below the chunk count) is one
   // of them, so every piece is read as is, with no per-lane select (5 VALU
   // instructions per chunk fewer in the VALU-bound decode loop).
   if (whole) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) st[nt] = *reinterpret_cast<const u32x4_t*>(lrow[nt] + kc * kKC);
+    for (int nt = 0; nt < NA; ++nt) st[nt] = *reinterpret_cast<const u32x4_t*>(lrow[nt] + kc * kKC);
     return;
   }
   const int lpiece = (threadIdx.x & 15) * 8;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int nt = 0; nt < NA; ++nt) {
     const bool ok = kc * kKC < kmax;
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lrow[nt] + (ok ? kc * kKC : -lpiece));
     const u32x4_t z = {0u, 0u, 0u, 0u};
@@ -91,11 +92,11 @@ __device__ __forceinline__ void load_b(u32x4_t (&st)[NT], const uint16_t* const 
   }
 }
 
-template <int NT>
+template <int NA, int NT>
 __device__ __forceinline__ void store_b(TileLds<NT>& lds, int buf, const u32x4_t (&st)[NT]) {
   const int r = threadIdx.x >> 4, piece = threadIdx.x & 15;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int nt = 0; nt < NA; ++nt)
     *reinterpret_cast<u32x4_t*>(&lds.b[buf][nt][r][piece * 8]) = st[nt];
 }
 
@@ -259,34 +260,51 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // prologue: weights of chunks 0 and 1, token tile of chunk 0
+    // three weight buffers and the token staging registers; k_loop first
+    // loads weights of chunks 0 and 1 and the token tile of chunk 0
     AFrag fr0, fr1, fr2;
     u32x4_t st[NT];
-    load_b<NT>(st, lrow, 0, kmax, whole);
-    load_a(fr0, wq, ws, lane);
-    load_a(fr1, Kc > 1 ? wq + cstride * (kMT * 64) : wq_dummy, Kc > 1 ? ws + cstride * 64 : ws_dummy,
-           lane);
-    __syncthreads();   // the previous pass's readers are done with the LDS tiles
-    store_b<NT>(lds, 0, st);
-    __syncthreads();
+    // token tiles that hold rows: the NT = 4 kernels load, store and compute
+    // only those (NT = 1 and 2 keep one body, all tiles; measured on the
+    // masked workload, loading only those tiles took W13 from 1383-1397 to
+    // 1354-1359 us)
+    const int nta = min(NT, (count - tb + 15) >> 4);   // uniform: count is the set's
+    auto with_live = [&](auto f) __attribute__((always_inline)) {
+      if constexpr (NT == 1 || NT == 2 || SET == SET_BLOCKS) {
+        f(std::integral_constant<int, NT>{});
+      } else {
+        static_assert(NT == 4, "token tiles per pass: 1, 2 or 4");
+        if (nta == 1) f(std::integral_constant<int, 1>{});
+        else if (nta == 2) f(std::integral_constant<int, 2>{});
+        else if (nta == 3) f(std::integral_constant<int, 3>{});
+        else f(std::integral_constant<int, 4>{});
+      }
+    };
 
     // step J computes chunk c from register buffer J and LDS buffer J, and
     // prefetches chunk c+2 into register buffer (J+2)%3 and the token tile of
-    // chunk c+1 into LDS buffer (J+1)%3. The MFMAs cover the pass's first NA
-    // token tiles, those that hold rows (the token loads stay whole).
+    // chunk c+1 into LDS buffer (J+1)%3. The loads, the LDS stores and the
+    // MFMAs cover the pass's first NA token tiles, those that hold rows.
     auto k_loop = [&](auto na) __attribute__((always_inline)) {
       constexpr int NA = decltype(na)::value;
+      load_b<NA, NT>(st, lrow, 0, kmax, whole);
+      load_a(fr0, wq, ws, lane);
+      load_a(fr1, Kc > 1 ? wq + cstride * (kMT * 64) : wq_dummy, Kc > 1 ? ws + cstride * 64 : ws_dummy,
+             lane);
+      __syncthreads();   // the previous pass's readers are done with the LDS tiles
+      store_b<NA, NT>(lds, 0, st);
+      __syncthreads();
 #define MOE_SMALL_M_STEP(J, CUR, NXT2)                                                           \
   {                                                                                              \
     const int c = kc + J;                                                                        \
-    load_b<NT>(st, lrow, min(c + 1, Kc - 1), kmax, whole);                                       \
+    load_b<NA, NT>(st, lrow, min(c + 1, Kc - 1), kmax, whole);                                   \
     const bool more = c + 2 < Kc;                                                                \
     load_a(NXT2, more ? wq + (size_t)(c + 2) * cstride * (kMT * 64) : wq_dummy,                  \
            more ? ws + (size_t)(c + 2) * cstride * 64 : ws_dummy, lane);                         \
     __builtin_amdgcn_sched_barrier(0);                                                           \
     if (c < Kc) mma_chunk<NA, NT>(CUR, lds, J, acc, mlo, mhi);                                   \
     __builtin_amdgcn_sched_barrier(0);                                                           \
-    store_b<NT>(lds, (J + 1) % 3, st);                                                           \
+    store_b<NA, NT>(lds, (J + 1) % 3, st);                                                       \
     __syncthreads();                                                                             \
   }
       // whole rotations, then the one or two chunks left (no step past the
@@ -307,16 +325,7 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
     // NT = 2 keeps one body: a second one does not fit its 168 registers
     // (3 workgroups per CU) without spilling; nor do four in the contiguous
     // blocks' BF16 store variant, whose rows are 128-row blocks anyway
-    const int nta = min(NT, (count - tb + 15) >> 4);   // uniform: count is the set's
-    if constexpr (NT == 1 || NT == 2 || SET == SET_BLOCKS) {
-      k_loop(std::integral_constant<int, NT>{});
-    } else {
-      static_assert(NT == 4, "token tiles per pass: 1, 2 or 4");
-      if (nta == 1) k_loop(std::integral_constant<int, 1>{});
-      else if (nta == 2) k_loop(std::integral_constant<int, 2>{});
-      else if (nta == 3) k_loop(std::integral_constant<int, 3>{});
-      else k_loop(std::integral_constant<int, 4>{});
-    }
+    with_live(k_loop);
     if (!active) continue;
 
     // ---- epilogue
@@ -672,14 +681,14 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m_jobs
   // the first
   AFrag fr0, fr1, fr2;
   u32x4_t st[NT];
-  load_b<NT>(st, lrow_cur, 0, kmax, whole);
+  load_b<NT, NT>(st, lrow_cur, 0, kmax, whole);
   load_a(fr0, cur.wq, cur.ws, lane);
   if (Kc > 1)
     load_a(fr1, cur.wq + kCh, cur.ws + 64, lane);
   else
     load_a(fr1, nxt.wq, nxt.ws, lane);
   __syncthreads();
-  store_b<NT>(lds, 0, st);
+  store_b<NT, NT>(lds, 0, st);
   __syncthreads();
 
   int c = 0;   // chunk of the current job computed by the next step
@@ -702,7 +711,7 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m_jobs
         _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) idv[nt] = pin(id_nxt[nt]);          \
         row_ptrs<NT, kGather>(p, idv, tp);                                                    \
       }                                                                                       \
-      load_b<NT>(st, tp, tcur ? c + 1 : 0, kmax, whole);                                      \
+      load_b<NT, NT>(st, tp, tcur ? c + 1 : 0, kmax, whole);                                  \
       const int w2 = c + 2;                                                                   \
       const bool wcur = w2 < Kc, wnxt = !wcur && w2 - Kc < Kc;                                \
       const int wc = wcur ? w2 : (wnxt ? w2 - Kc : 0);                                        \
@@ -738,7 +747,7 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m_jobs
       }                                                                                       \
       live = cur.j < js.j1;                                                                   \
     }                                                                                         \
-    store_b<NT>(lds, (J + 1) % 3, st);                                                        \
+    store_b<NT, NT>(lds, (J + 1) % 3, st);                                                    \
     __syncthreads();                                                                          \
   }
   while (live) {
