@@ -92,6 +92,34 @@ __device__ __forceinline__ void load_b(u32x4_t (&st)[NT], const uint16_t* const 
   }
 }
 
+// load_b for the rows a set holds only: a lane whose token row lies past
+// them keeps its registers (zero from the pass start) and sends no request.
+// Those rows' MFMA columns are never stored. Used by the one-tile kernels
+// of the first GEMM, whose rows are gathered (decode: ~9 of 16 rows hold
+// tokens; W13 1066-1074 -> 1055-1062 us). The second GEMM's rows are
+// consecutive, so its padding rows cost little (W2 measured 3 us slower
+// with it), and in the four-tile kernels the per-tile lane branches cost
+// more than the loads they save (masked W13 1346 -> 1428 us).
+template <int NT>
+__device__ __forceinline__ void load_b_rows(u32x4_t (&st)[NT], const uint16_t* const (&lrow)[NT],
+                                            const bool (&rv)[NT], int kc, int kmax, bool whole) {
+  if (whole) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      if (rv[nt]) st[nt] = *reinterpret_cast<const u32x4_t*>(lrow[nt] + kc * kKC);
+    return;
+  }
+  const int lpiece = (threadIdx.x & 15) * 8;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (!rv[nt]) continue;
+    const bool ok = kc * kKC < kmax;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lrow[nt] + (ok ? kc * kKC : -lpiece));
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    st[nt] = ok ? v : z;
+  }
+}
+
 template <int NA, int NT>
 __device__ __forceinline__ void store_b(TileLds<NT>& lds, int buf, const u32x4_t (&st)[NT]) {
   const int r = threadIdx.x >> 4, piece = threadIdx.x & 15;
@@ -243,14 +271,17 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
 
   for (int tb = 0; tb < count; tb += 16 * NT) {
     const uint16_t* lrow[NT];
+    bool rv[NT];   // the lane's token row holds a row of the set (one-tile first GEMM)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int r = min(tb + nt * 16 + lr, count - 1);   // pad columns repeat a valid row
       const int slot = slot0 + r;
       int row = slot;
+      rv[nt] = tb + nt * 16 + lr < count;
       if (gather) {
         const int f = p.sorted_ids[slot];
         row = (f >= 0 && f < p.sentinel) ? f / p.topk : 0;   // pad slots read row 0
+        rv[nt] = rv[nt] && f >= 0 && f < p.sentinel;
       }
       lrow[nt] = p.src + (size_t)row * p.src_ld + c0 * kKC + lpiece;
     }
@@ -264,6 +295,14 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
     // loads weights of chunks 0 and 1 and the token tile of chunk 0
     AFrag fr0, fr1, fr2;
     u32x4_t st[NT];
+    constexpr bool kRowsOnly = NT == 1 && EPI == EPI_SWIGLU;
+    if constexpr (kRowsOnly) st[0] = u32x4_t{0u, 0u, 0u, 0u};
+    // one chunk's token rows: all rows of the first NA tiles, or (one-tile
+    // first GEMM) only the rows the set holds
+    auto load_tokens = [&](auto na, int kc) __attribute__((always_inline)) {
+      if constexpr (kRowsOnly) load_b_rows<NT>(st, lrow, rv, kc, kmax, whole);
+      else load_b<decltype(na)::value, NT>(st, lrow, kc, kmax, whole);
+    };
     // token tiles that hold rows: the NT = 4 kernels load, store and compute
     // only those (NT = 1 and 2 keep one body, all tiles; measured on the
     // masked workload, loading only those tiles took W13 from 1383-1397 to
@@ -287,7 +326,7 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
     // MFMAs cover the pass's first NA token tiles, those that hold rows.
     auto k_loop = [&](auto na) __attribute__((always_inline)) {
       constexpr int NA = decltype(na)::value;
-      load_b<NA, NT>(st, lrow, 0, kmax, whole);
+      load_tokens(na, 0);
       load_a(fr0, wq, ws, lane);
       load_a(fr1, Kc > 1 ? wq + cstride * (kMT * 64) : wq_dummy, Kc > 1 ? ws + cstride * 64 : ws_dummy,
              lane);
@@ -297,7 +336,7 @@ __global__ __launch_bounds__(256, kSmallMBlocksPerCU<NT>) void gemm_small_m(cons
 #define MOE_SMALL_M_STEP(J, CUR, NXT2)                                                           \
   {                                                                                              \
     const int c = kc + J;                                                                        \
-    load_b<NA, NT>(st, lrow, min(c + 1, Kc - 1), kmax, whole);                                   \
+    load_tokens(na, min(c + 1, Kc - 1));                                                         \
     const bool more = c + 2 < Kc;                                                                \
     load_a(NXT2, more ? wq + (size_t)(c + 2) * cstride * (kMT * 64) : wq_dummy,                  \
            more ? ws + (size_t)(c + 2) * cstride * 64 : ws_dummy, lane);                         \
