@@ -22,7 +22,9 @@
 //     keep HBM busy at four waves per SIMD);
 //   * the workgroup loads the token tile (16*NT rows x 128 k of BF16) once,
 //     one chunk ahead, through registers into one of three LDS buffers
-//     (rows padded to 272 B so the fragment reads hit 64 distinct banks);
+//     (rows padded to 272 B so the fragment reads hit 64 distinct banks):
+//     with four tiles only the tiles that hold rows, with one tile in the
+//     first GEMM only the rows the expert holds;
 //   * every lane's 32 k values of a tile share one scale group, so each
 //     (lane, tile, chunk) needs one scale.
 // Loads past the last chunk go to a valid dummy address, so every load in
